@@ -1,0 +1,214 @@
+// C ABI entry points of libmoe: host-side argument validation, workspace
+// carving and kernel launches.  No entry point allocates, frees, copies to
+// the host or synchronises; everything is enqueued on the caller's stream.
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+constexpr int64_t kMaxRows = (int64_t)1 << 31;
+
+// common validation of a grouped GEMM shape; returns MOE_OK or an error
+int check_gemm_shape(int dtype, const int32_t* group_off, int capacity, int E, int64_t n_rows,
+                     int d, int f)
+{
+    if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_MXFP8) return MOE_EUNSUPPORTED;
+    if (E < 1 || E > kMaxExperts || n_rows < 0 || n_rows >= kMaxRows || d < 1 || f < 1 ||
+        capacity < 0)
+        return MOE_EINVAL;
+    if (capacity > 0 && (int64_t)E * capacity != n_rows) return MOE_EINVAL;
+    if (capacity == 0 && !group_off) return MOE_EINVAL;
+    const int unit = dtype == MOE_MXFP8 ? 32 : (dtype == MOE_F32 ? 4 : 8);
+    if (d % unit || f % unit) return MOE_EALIGN;
+    if (n_rows * (int64_t)(d > 2 * f ? d : 2 * f) >= ((int64_t)1 << 40)) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_version(void) { return 100; }
+
+const char* moe_status_string(int status)
+{
+    switch (status) {
+    case MOE_OK: return "MOE_OK: success";
+    case MOE_EINVAL: return "MOE_EINVAL: null pointer or invalid / inconsistent size";
+    case MOE_EALIGN: return "MOE_EALIGN: row width or pointer alignment not supported";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: dtype or option combination not provided";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace missing or too small";
+    case MOE_EHIP: return "MOE_EHIP: kernel launch failed";
+    default: return "unknown moe status";
+    }
+}
+
+size_t moe_route_workspace_bytes(int T, int E, int k)
+{
+    if (T < 0 || E < 1 || k < 1) return 0;
+    const size_t nblk = ((size_t)T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock;
+    return align_up((size_t)T * k * sizeof(int32_t)) + align_up(nblk * E * sizeof(int32_t)) + kAlign;
+}
+
+int moe_route_topk(const float* logits, int T, int E, int k, int capacity, int32_t* topk_idx,
+                   float* topk_w, int32_t* counts, int32_t* offsets, int32_t* dst_row,
+                   int32_t* src_slot, int64_t n_rows, void* ws, size_t ws_bytes,
+                   int32_t* dev_err, moe_stream_t stream)
+{
+    if (T < 0 || E < 1 || E > kMaxExperts || k < 1 || k > kMaxTopK || k > E || capacity < 0)
+        return MOE_EINVAL;
+    if ((int64_t)T * k >= kMaxRows || (int64_t)E * capacity >= kMaxRows) return MOE_EINVAL;
+    const int64_t want_rows = capacity > 0 ? (int64_t)E * capacity : (int64_t)T * k;
+    if (n_rows != want_rows) return MOE_EINVAL;
+    if (!counts || !offsets) return MOE_EINVAL;
+    if (T > 0 && (!logits || !topk_idx || !topk_w || !dst_row)) return MOE_EINVAL;
+    if (n_rows > 0 && !src_slot) return MOE_EINVAL;
+    const size_t need = moe_route_workspace_bytes(T, E, k);
+    if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+    // carve: lrank [T*k], hist [nblk*E]
+    uint8_t* base = reinterpret_cast<uint8_t*>(
+        (reinterpret_cast<uintptr_t>(ws) + kAlign - 1) / kAlign * kAlign);
+    int32_t* lrank = reinterpret_cast<int32_t*>(base);
+    int32_t* hist = reinterpret_cast<int32_t*>(base + align_up((size_t)T * k * sizeof(int32_t)));
+    return status_of(launch_route(logits, T, E, k, capacity, topk_idx, topk_w, counts, offsets,
+                                  dst_row, src_slot, n_rows, lrank, hist, dev_err,
+                                  as_stream(stream)));
+}
+
+int moe_permute(int dtype, const void* x, int T, int d, int k, const int32_t* dst_row,
+                const int32_t* src_slot, const float* row_scale, int64_t n_rows, void* x_perm,
+                uint8_t* x_perm_scales, int32_t* dev_err, moe_stream_t stream)
+{
+    if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_MXFP8) return MOE_EUNSUPPORTED;
+    if (T < 0 || d < 1 || k < 1 || k > kMaxTopK || n_rows < 0 || n_rows >= kMaxRows)
+        return MOE_EINVAL;
+    if ((int64_t)T * k >= kMaxRows) return MOE_EINVAL;
+    const bool padded = n_rows != (int64_t)T * k;
+    if (T > 0 && (!x || !dst_row)) return MOE_EINVAL;
+    if (n_rows > 0 && !x_perm) return MOE_EINVAL;
+    if (padded && n_rows > 0 && !src_slot) return MOE_EINVAL;
+    const int unit = dtype == MOE_MXFP8 ? 32 : (dtype == MOE_F32 ? 4 : 8);
+    if (d % unit) return MOE_EALIGN;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_EALIGN;
+    if (dtype == MOE_MXFP8) {
+        if (row_scale) return MOE_EUNSUPPORTED;
+        if (n_rows > 0 && !x_perm_scales) return MOE_EINVAL;
+    }
+    return status_of(launch_permute(dtype, x, T, d, k, dst_row, src_slot, row_scale, n_rows,
+                                    x_perm, x_perm_scales, dev_err, as_stream(stream)));
+}
+
+int moe_unpermute_combine(int dtype, const void* y_perm, const int32_t* dst_row,
+                          const float* weights, int T, int k, int d, int64_t n_rows, void* out,
+                          int32_t* dev_err, moe_stream_t stream)
+{
+    if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+    if (T < 0 || d < 1 || k < 1 || k > kMaxTopK || n_rows < 0 || n_rows >= kMaxRows)
+        return MOE_EINVAL;
+    if (T > 0 && (!dst_row || !out || (n_rows > 0 && !y_perm))) return MOE_EINVAL;
+    const int unit = dtype == MOE_F32 ? 4 : 8;
+    if (d % unit) return MOE_EALIGN;
+    if (!aligned16(y_perm) || !aligned16(out)) return MOE_EALIGN;
+    return status_of(launch_combine(dtype, y_perm, dst_row, weights, T, k, d, n_rows, out, dev_err,
+                                    as_stream(stream)));
+}
+
+size_t moe_gemm_workspace_bytes(int dtype, int E, int64_t n_rows, int d, int f)
+{
+    if (dtype != MOE_MXFP8) return 0;
+    if (E < 1 || n_rows < 0 || d < 1 || f < 1) return 0;
+    return gemm_ws_mxfp8(E, n_rows, d, f);
+}
+
+int moe_grouped_gemm_fwd(int dtype, const void* x_perm, const uint8_t* x_perm_scales,
+                         const void* w13, const uint8_t* w13_scales, const void* w2,
+                         const uint8_t* w2_scales, const int32_t* group_off, int capacity, int E,
+                         int64_t n_rows, int d, int f, void* gu, void* h, void* y_perm, void* ws,
+                         size_t ws_bytes, moe_stream_t stream)
+{
+    int st = check_gemm_shape(dtype, group_off, capacity, E, n_rows, d, f);
+    if (st != MOE_OK) return st;
+    if (!w13 || !w2) return MOE_EINVAL;
+    if (n_rows > 0 && (!x_perm || !gu || !h || !y_perm)) return MOE_EINVAL;
+    for (const void* p : {x_perm, w13, w2, (const void*)gu, (const void*)h, (const void*)y_perm})
+        if (!aligned16(p)) return MOE_EALIGN;
+    GroupSpec g{capacity > 0 ? nullptr : group_off, capacity, E, n_rows};
+    hipStream_t s = as_stream(stream);
+    if (dtype == MOE_F32)
+        return status_of(gemm_fwd_f32((const float*)x_perm, (const float*)w13, (const float*)w2, g,
+                                      d, f, (float*)gu, (float*)h, (float*)y_perm, s));
+    if (dtype == MOE_BF16)
+        return status_of(gemm_fwd_bf16((const uint16_t*)x_perm, (const uint16_t*)w13,
+                                       (const uint16_t*)w2, g, d, f, (uint16_t*)gu, (uint16_t*)h,
+                                       (uint16_t*)y_perm, s));
+    if (!x_perm_scales || !w13_scales || !w2_scales) return MOE_EINVAL;
+    const size_t need = moe_gemm_workspace_bytes(dtype, E, n_rows, d, f);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
+    return status_of(gemm_fwd_mxfp8((const uint8_t*)x_perm, x_perm_scales, (const uint8_t*)w13,
+                                    w13_scales, (const uint8_t*)w2, w2_scales, g, d, f,
+                                    (uint16_t*)gu, (uint16_t*)h, (uint16_t*)y_perm, ws, s));
+}
+
+int moe_grouped_gemm_bwd(int dtype, const void* dy_perm, const void* x_perm,
+                         const uint8_t* x_perm_scales, const void* gu, const void* h,
+                         const void* w13, const uint8_t* w13_scales, const void* w2,
+                         const uint8_t* w2_scales, const int32_t* group_off, int capacity, int E,
+                         int64_t n_rows, int d, int f, void* dgu, void* dx_perm, void* dw13,
+                         void* dw2, void* ws, size_t ws_bytes, moe_stream_t stream)
+{
+    int st = check_gemm_shape(dtype, group_off, capacity, E, n_rows, d, f);
+    if (st != MOE_OK) return st;
+    if (!w13 || !w2 || !dw13 || !dw2) return MOE_EINVAL;
+    if (n_rows > 0 && (!dy_perm || !x_perm || !gu || !h || !dgu || !dx_perm)) return MOE_EINVAL;
+    for (const void* p : {dy_perm, x_perm, gu, h, w13, w2, (const void*)dgu, (const void*)dx_perm,
+                          (const void*)dw13, (const void*)dw2})
+        if (!aligned16(p)) return MOE_EALIGN;
+    GroupSpec g{capacity > 0 ? nullptr : group_off, capacity, E, n_rows};
+    hipStream_t s = as_stream(stream);
+    if (dtype == MOE_F32)
+        return status_of(gemm_bwd_f32((const float*)dy_perm, (const float*)x_perm,
+                                      (const float*)gu, (const float*)h, (const float*)w13,
+                                      (const float*)w2, g, d, f, (float*)dgu, (float*)dx_perm,
+                                      (float*)dw13, (float*)dw2, s));
+    if (dtype == MOE_BF16)
+        return status_of(gemm_bwd_bf16((const uint16_t*)dy_perm, (const uint16_t*)x_perm,
+                                       (const uint16_t*)gu, (const uint16_t*)h,
+                                       (const uint16_t*)w13, (const uint16_t*)w2, g, d, f,
+                                       (uint16_t*)dgu, (uint16_t*)dx_perm, (uint16_t*)dw13,
+                                       (uint16_t*)dw2, s));
+    if (!x_perm_scales || !w13_scales || !w2_scales) return MOE_EINVAL;
+    const size_t need = moe_gemm_workspace_bytes(dtype, E, n_rows, d, f);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
+    return status_of(gemm_bwd_mxfp8((const uint16_t*)dy_perm, (const uint8_t*)x_perm,
+                                    x_perm_scales, (const uint16_t*)gu, (const uint16_t*)h,
+                                    (const uint8_t*)w13, w13_scales, (const uint8_t*)w2,
+                                    w2_scales, g, d, f, (uint16_t*)dgu, (uint16_t*)dx_perm,
+                                    (uint16_t*)dw13, (uint16_t*)dw2, ws, s));
+}
+
+int moe_quantize_mxfp8(const void* src, int64_t rows, int K, int colwise, const int32_t* group_off,
+                       int n_groups, uint8_t* codes, uint8_t* scales, moe_stream_t stream)
+{
+    if (rows < 0 || rows >= kMaxRows || K < 1) return MOE_EINVAL;
+    if (rows > 0 && (!src || !codes || !scales)) return MOE_EINVAL;
+    if (!aligned16(src) || !aligned16(codes)) return MOE_EALIGN;
+    hipStream_t s = as_stream(stream);
+    if (!colwise) {
+        if (K % 32) return MOE_EALIGN;
+        return status_of(launch_quantize_rows((const uint16_t*)src, rows, K, codes, scales, s));
+    }
+    if (group_off && (n_groups < 1 || n_groups > kMaxExperts)) return MOE_EINVAL;
+    return status_of(launch_quantize_cols((const uint16_t*)src, rows, K, group_off, 0,
+                                          group_off ? n_groups : 1, codes, scales, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,398 @@
+// Rowwise dispatch (permute), un-permute/combine, and the MXFP8 quantisers.
+//
+// Permute follows the OLMo-core 3 tutorial's "rowwise EP" paragraph: each
+// token row is written straight into the row of its expert's input buffer
+// given by the route map; there is no pack step.  The kernel reads each
+// token row once (16-byte loads) and writes it to its k destinations
+// (16-byte stores); the combine reads the k rows of a token and writes one.
+// All HBM accesses are whole 16-byte vectors, consecutive lanes on
+// consecutive vectors of the same row.
+//
+// MXFP8 (tutorial, MXFP8 section): one E8M0 scale per 32 elements, the
+// smallest power of two that keeps the block maximum within 448, codes by
+// round-to-nearest-even into E4M3FN.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// 8 x bf16 or 4 x fp32 per 16-byte vector
+template <bool BF16>
+__device__ __forceinline__ uint4 scale_vec(uint4 v, float s)
+{
+    if constexpr (BF16) {
+        uint4 o;
+        o.x = pack_bf16x2(s * bf16_lo(v.x), s * bf16_hi(v.x));
+        o.y = pack_bf16x2(s * bf16_lo(v.y), s * bf16_hi(v.y));
+        o.z = pack_bf16x2(s * bf16_lo(v.z), s * bf16_hi(v.z));
+        o.w = pack_bf16x2(s * bf16_lo(v.w), s * bf16_hi(v.w));
+        return o;
+    } else {
+        uint4 o;
+        o.x = __float_as_uint(s * __uint_as_float(v.x));
+        o.y = __float_as_uint(s * __uint_as_float(v.y));
+        o.z = __float_as_uint(s * __uint_as_float(v.z));
+        o.w = __float_as_uint(s * __uint_as_float(v.w));
+        return o;
+    }
+}
+
+// thread i handles vector (i % nvec) of token row (i / nvec)
+template <bool BF16, bool SCALE>
+__global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x, int T, int nvec,
+                                                      int k, const int32_t* __restrict__ dst_row,
+                                                      const float* __restrict__ row_scale,
+                                                      int64_t n_rows, uint4* __restrict__ x_perm,
+                                                      int32_t* __restrict__ dev_err)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)T * nvec) return;
+    const int64_t t = i / nvec;
+    const int v = (int)(i - t * nvec);
+    const uint4 val = x[i];
+    bool bad = false;
+    for (int j = 0; j < k; ++j) {
+        const int64_t dst = dst_row[t * k + j];
+        if (dst < 0) continue;
+        if (dst >= n_rows) {
+            bad = true;
+            continue;
+        }
+        uint4 o = val;
+        if constexpr (SCALE) o = scale_vec<BF16>(val, row_scale[t * k + j]);
+        x_perm[dst * nvec + v] = o;
+    }
+    if (bad && dev_err) atomicOr(dev_err, (int)MOE_ERR_ROW_RANGE);
+}
+
+// zero the rows nobody fills (padded layout); 16 rows per block
+__global__ __launch_bounds__(256) void zero_rows_kernel(const int32_t* __restrict__ src_slot,
+                                                        int64_t n_rows, int nvec,
+                                                        uint4* __restrict__ buf,
+                                                        uint8_t* __restrict__ scales, int nsc)
+{
+    const int64_t r0 = (int64_t)blockIdx.x * 16;
+    for (int64_t r = r0; r < r0 + 16 && r < n_rows; ++r) {
+        if (src_slot[r] >= 0) continue;
+        for (int v = threadIdx.x; v < nvec; v += 256) buf[r * nvec + v] = make_uint4(0, 0, 0, 0);
+        if (scales)
+            for (int b = threadIdx.x; b < nsc; b += 256) scales[r * nsc + b] = 0;
+    }
+}
+
+// quantise 32 bf16 (four 16-byte vectors) into 32 E4M3FN codes + scale exponent
+__device__ __forceinline__ int quant32(const uint4 (&in)[4], uint4 (&out)[2])
+{
+    float vals[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t w[4] = {in[q].x, in[q].y, in[q].z, in[q].w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            vals[q * 8 + 2 * p] = bf16_lo(w[p]);
+            vals[q * 8 + 2 * p + 1] = bf16_hi(w[p]);
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(vals[i]));
+    const int e = mx_scale_exp(amax);
+    uint32_t c[8];
+#pragma unroll
+    for (int wi = 0; wi < 8; ++wi) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            // ldexp keeps the exact product even when 2^-e overflows fp32 (e = -127)
+            const float q = __builtin_ldexpf(vals[wi * 4 + b], -e);
+            word |= f32_to_e4m3(q) << (8 * b);
+        }
+        c[wi] = word;
+    }
+    out[0] = make_uint4(c[0], c[1], c[2], c[3]);
+    out[1] = make_uint4(c[4], c[5], c[6], c[7]);
+    return e;
+}
+
+// MXFP8 dispatch: thread i quantises 32-element block (i % nblk32) of token row
+// (i / nblk32) and writes it to the k destinations
+__global__ __launch_bounds__(256) void permute_mx_kernel(const uint4* __restrict__ x, int T,
+                                                         int nb32, int k,
+                                                         const int32_t* __restrict__ dst_row,
+                                                         int64_t n_rows, uint4* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales,
+                                                         int32_t* __restrict__ dev_err)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)T * nb32) return;
+    const int64_t t = i / nb32;
+    const int b = (int)(i - t * nb32);
+    uint4 in[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) in[q] = x[i * 4 + q];
+    uint4 out[2];
+    const int e = quant32(in, out);
+    bool bad = false;
+    for (int j = 0; j < k; ++j) {
+        const int64_t dst = dst_row[t * k + j];
+        if (dst < 0) continue;
+        if (dst >= n_rows) {
+            bad = true;
+            continue;
+        }
+        codes[(dst * nb32 + b) * 2] = out[0];
+        codes[(dst * nb32 + b) * 2 + 1] = out[1];
+        scales[dst * nb32 + b] = (uint8_t)(e + 127);
+    }
+    if (bad && dev_err) atomicOr(dev_err, (int)MOE_ERR_ROW_RANGE);
+}
+
+// row-wise quantiser: thread i handles block (i % nb32) of row (i / nb32)
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint4* __restrict__ src,
+                                                         int64_t rows, int nb32,
+                                                         uint4* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= rows * nb32) return;
+    uint4 in[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) in[q] = src[i * 4 + q];
+    uint4 out[2];
+    const int e = quant32(in, out);
+    codes[i * 2] = out[0];
+    codes[i * 2 + 1] = out[1];
+    scales[i] = (uint8_t)(e + 127);
+}
+
+// Column-wise quantiser inside row groups.  Block (cb, L): columns
+// [cb*256, cb*256+256) of the L-th 32-row block in the concatenation of all
+// groups' padded row blocks (device schedule from the group offsets).  Each
+// thread quantises one column over those 32 rows and writes the 32 codes as
+// one 32-byte run of the transposed group layout.
+template <bool FROM_MX>
+__global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restrict__ src,
+                                                         const uint8_t* __restrict__ src_codes,
+                                                         const uint8_t* __restrict__ src_scales,
+                                                         int64_t rows, int K,
+                                                         const int32_t* __restrict__ group_off,
+                                                         int capacity, int n_groups,
+                                                         uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales)
+{
+    __shared__ int s_pref[kMaxExperts + 1];
+    __shared__ int s_part[256];
+    int g = 0, rb = blockIdx.y;
+    int64_t g0 = 0, g1 = rows, P = 0;
+    if (group_off || capacity > 0) {
+        const int total =
+            block_tile_prefix<256>(group_off, capacity, n_groups, rows, 32, 1, s_pref, s_part);
+        if ((int)blockIdx.y >= total) return;
+        g = find_group(s_pref, n_groups, blockIdx.y);
+        rb = blockIdx.y - s_pref[g];
+        g0 = group_begin(group_off, capacity, g, rows);
+        g1 = g0 + group_rows(group_off, capacity, g, rows);
+        P = (int64_t)s_pref[g] * 32;              // padded rows of earlier groups
+    } else if ((int64_t)rb * 32 >= rows) {
+        return;
+    }
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= K) return;
+    const int64_t mpad = (g1 - g0 + 31) / 32 * 32;
+    float vals[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+        const int64_t row = g0 + (int64_t)rb * 32 + r;
+        float v = 0.0f;
+        if (row < g1) {
+            if constexpr (FROM_MX) {
+                const uint32_t code = src_codes[row * K + c];
+                const int se = (int)src_scales[row * (K / 32) + c / 32] - 127;
+                const int ex = (code >> 3) & 0xF, mt = code & 7;
+                const float a = ex == 0 ? (float)mt * 0.001953125f : __builtin_ldexpf(8.0f + mt, ex - 10);
+                v = __builtin_ldexpf((code & 0x80) ? -a : a, se);
+            } else {
+                v = bf16_to_f32(src[row * K + c]);
+            }
+        }
+        vals[r] = v;
+        amax = fmaxf(amax, fabsf(v));
+    }
+    const int e = mx_scale_exp(amax);
+    uint32_t w[8];
+#pragma unroll
+    for (int wi = 0; wi < 8; ++wi) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) word |= f32_to_e4m3(__builtin_ldexpf(vals[wi * 4 + b], -e)) << (8 * b);
+        w[wi] = word;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(codes + (int64_t)K * P + (int64_t)c * mpad + rb * 32);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    scales[(int64_t)K * P / 32 + (int64_t)c * (mpad / 32) + rb] = (uint8_t)(e + 127);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y,
+                                                      const int32_t* __restrict__ dst_row,
+                                                      const float* __restrict__ w, int T, int k,
+                                                      int nvec, int64_t n_rows,
+                                                      uint4* __restrict__ out,
+                                                      int32_t* __restrict__ dev_err)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)T * nvec) return;
+    const int64_t t = i / nvec;
+    const int v = (int)(i - t * nvec);
+    constexpr int NE = BF16 ? 8 : 4;
+    float acc[NE];
+#pragma unroll
+    for (int q = 0; q < NE; ++q) acc[q] = 0.0f;
+    bool bad = false;
+    for (int j = 0; j < k; ++j) {
+        const int64_t dst = dst_row[t * k + j];
+        if (dst < 0) continue;
+        if (dst >= n_rows) {
+            bad = true;
+            continue;
+        }
+        const float wt = w ? w[t * k + j] : 1.0f;
+        const uint4 val = y[dst * nvec + v];
+        const uint32_t ww[4] = {val.x, val.y, val.z, val.w};
+        if constexpr (BF16) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                acc[2 * p] = fmaf(wt, bf16_lo(ww[p]), acc[2 * p]);
+                acc[2 * p + 1] = fmaf(wt, bf16_hi(ww[p]), acc[2 * p + 1]);
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) acc[p] = fmaf(wt, __uint_as_float(ww[p]), acc[p]);
+        }
+    }
+    uint4 o;
+    if constexpr (BF16) {
+        o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                       pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    } else {
+        o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                       __float_as_uint(acc[3]));
+    }
+    out[i] = o;
+    if (bad && dev_err) atomicOr(dev_err, (int)MOE_ERR_ROW_RANGE);
+}
+
+inline unsigned grid_for(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+}  // namespace
+
+hipError_t launch_permute(int dtype, const void* x, int T, int d, int k, const int32_t* dst_row,
+                          const int32_t* src_slot, const float* row_scale, int64_t n_rows,
+                          void* x_perm, uint8_t* x_scales, int32_t* dev_err, hipStream_t s)
+{
+    const bool padded = n_rows != (int64_t)T * k;
+    if (dtype == MOE_MXFP8) {
+        const int nb32 = d / 32;
+        const int64_t n = (int64_t)T * nb32;
+        if (n > 0)
+            hipLaunchKernelGGL(permute_mx_kernel, dim3(grid_for(n)), dim3(256), 0, s,
+                               (const uint4*)x, T, nb32, k, dst_row, n_rows, (uint4*)x_perm,
+                               x_scales, dev_err);
+        if (padded && n_rows > 0)
+            hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)((n_rows + 15) / 16)), dim3(256), 0,
+                               s, src_slot, n_rows, d / 16, (uint4*)x_perm, x_scales, nb32);
+        return hipGetLastError();
+    }
+    const bool bf = dtype == MOE_BF16;
+    const int nvec = bf ? d / 8 : d / 4;
+    const int64_t n = (int64_t)T * nvec;
+    if (n > 0) {
+        const dim3 grid(grid_for(n)), blk(256);
+        if (bf && row_scale)
+            hipLaunchKernelGGL((permute_kernel<true, true>), grid, blk, 0, s, (const uint4*)x, T,
+                               nvec, k, dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
+        else if (bf)
+            hipLaunchKernelGGL((permute_kernel<true, false>), grid, blk, 0, s, (const uint4*)x, T,
+                               nvec, k, dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
+        else if (row_scale)
+            hipLaunchKernelGGL((permute_kernel<false, true>), grid, blk, 0, s, (const uint4*)x, T,
+                               nvec, k, dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
+        else
+            hipLaunchKernelGGL((permute_kernel<false, false>), grid, blk, 0, s, (const uint4*)x, T,
+                               nvec, k, dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
+    }
+    if (padded && n_rows > 0)
+        hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)((n_rows + 15) / 16)), dim3(256), 0, s,
+                           src_slot, n_rows, nvec, (uint4*)x_perm, (uint8_t*)nullptr, 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* dst_row, const float* w,
+                          int T, int k, int d, int64_t n_rows, void* out, int32_t* dev_err,
+                          hipStream_t s)
+{
+    const bool bf = dtype == MOE_BF16;
+    const int nvec = bf ? d / 8 : d / 4;
+    const int64_t n = (int64_t)T * nvec;
+    if (n > 0) {
+        if (bf)
+            hipLaunchKernelGGL((combine_kernel<true>), dim3(grid_for(n)), dim3(256), 0, s,
+                               (const uint4*)y_perm, dst_row, w, T, k, nvec, n_rows, (uint4*)out,
+                               dev_err);
+        else
+            hipLaunchKernelGGL((combine_kernel<false>), dim3(grid_for(n)), dim3(256), 0, s,
+                               (const uint4*)y_perm, dst_row, w, T, k, nvec, n_rows, (uint4*)out,
+                               dev_err);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows(const uint16_t* src, int64_t rows, int K, uint8_t* codes,
+                                uint8_t* scales, hipStream_t s)
+{
+    const int nb32 = K / 32;
+    const int64_t n = rows * nb32;
+    if (n > 0)
+        hipLaunchKernelGGL(quant_rows_kernel, dim3(grid_for(n)), dim3(256), 0, s,
+                           (const uint4*)src, rows, nb32, (uint4*)codes, scales);
+    return hipGetLastError();
+}
+
+static hipError_t launch_cols(bool from_mx, const uint16_t* src, const uint8_t* sc,
+                              const uint8_t* ss, int64_t rows, int K, const int32_t* group_off,
+                              int capacity, int n_groups, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s)
+{
+    // bound on the number of 32-row blocks over all groups
+    const int64_t nrb = rows / 32 + (group_off || capacity > 0 ? n_groups : 1);
+    if (nrb == 0 || K == 0) return hipGetLastError();
+    const dim3 grid((unsigned)((K + 255) / 256), (unsigned)nrb);
+    if (from_mx)
+        hipLaunchKernelGGL((quant_cols_kernel<true>), grid, dim3(256), 0, s, src, sc, ss, rows, K,
+                           group_off, capacity, n_groups, codes, scales);
+    else
+        hipLaunchKernelGGL((quant_cols_kernel<false>), grid, dim3(256), 0, s, src, sc, ss, rows, K,
+                           group_off, capacity, n_groups, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_cols(const uint16_t* src, int64_t rows, int K, const int32_t* group_off,
+                                int capacity, int n_groups, uint8_t* codes, uint8_t* scales,
+                                hipStream_t s)
+{
+    return launch_cols(false, src, nullptr, nullptr, rows, K, group_off, capacity, n_groups, codes,
+                       scales, s);
+}
+
+hipError_t launch_dequant_requant_cols(const uint8_t* codes_row, const uint8_t* scales_row,
+                                       int64_t rows, int K, const int32_t* group_off,
+                                       int capacity, int n_groups, uint8_t* codes,
+                                       uint8_t* scales, hipStream_t s)
+{
+    return launch_cols(true, nullptr, codes_row, scales_row, rows, K, group_off, capacity,
+                       n_groups, codes, scales, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,146 @@
+"""One MoE feed-forward layer on one GPU, sequenced over the C ABI.
+
+``MoELayer`` owns the device buffers of one layer shape and issues the ABI
+calls in the order of the method (route -> permute -> grouped GEMM forward ->
+combine, then the backward twins), all on one stream with no host
+synchronisation.  It does no arithmetic of its own: every step runs in the
+HIP library.  Buffers come from torch's caching allocator.
+
+The backward of the layer with the routing held fixed:
+    dy_perm = permute(dout, row_scale = topk_w)     (combine backward)
+    dgu, dx_perm, dw13, dw2 = grouped_gemm_bwd(...)
+    dx = unpermute_combine(dx_perm, weights = None) (permute backward)
+"""
+import torch
+
+from . import (MOE_BF16, MOE_F32, MOE_MXFP8, moe_gemm_workspace_bytes, moe_grouped_gemm_bwd,
+               moe_grouped_gemm_fwd, moe_permute, moe_quantize_mxfp8, moe_route_topk,
+               moe_route_workspace_bytes, moe_unpermute_combine)
+
+_ACT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_MXFP8: torch.bfloat16}
+
+
+class MoELayer:
+    def __init__(self, T, d, E, f, k, dtype=MOE_BF16, capacity=0, device="cuda"):
+        self.T, self.d, self.E, self.f, self.k = T, d, E, f, k
+        self.dtype, self.capacity, self.device = dtype, capacity, device
+        self.n_rows = E * capacity if capacity > 0 else T * k
+        R = self.n_rows
+        act = _ACT[dtype]
+        i32 = dict(dtype=torch.int32, device=device)
+        self.topk_idx = torch.empty(T, k, **i32)
+        self.topk_w = torch.empty(T, k, dtype=torch.float32, device=device)
+        self.counts = torch.empty(E, **i32)
+        self.offsets = torch.empty(E + 1, **i32)
+        self.dst_row = torch.empty(T * k, **i32)
+        self.src_slot = torch.empty(R, **i32)
+        self.dev_err = torch.zeros(1, **i32)
+        self.route_ws = torch.empty(moe_route_workspace_bytes(T, E, k), dtype=torch.uint8,
+                                    device=device)
+        if dtype == MOE_MXFP8:
+            self.x_perm = torch.empty(R, d, dtype=torch.uint8, device=device)
+            self.x_perm_scales = torch.empty(R, d // 32, dtype=torch.uint8, device=device)
+        else:
+            self.x_perm = torch.empty(R, d, dtype=act, device=device)
+            self.x_perm_scales = None
+        self.gu = torch.empty(R, 2 * f, dtype=act, device=device)
+        self.h = torch.empty(R, f, dtype=act, device=device)
+        self.y_perm = torch.empty(R, d, dtype=act, device=device)
+        self.out = torch.empty(T, d, dtype=act, device=device)
+        self.gemm_ws = None
+        wsb = moe_gemm_workspace_bytes(dtype, E, R, d, f)
+        if wsb:
+            self.gemm_ws = torch.empty(wsb, dtype=torch.uint8, device=device)
+        self._bwd_alloc = False
+
+    def _alloc_bwd(self):
+        if self._bwd_alloc:
+            return
+        R, d, f, E = self.n_rows, self.d, self.f, self.E
+        act = _ACT[self.dtype]
+        dev = self.device
+        self.dy_perm = torch.empty(R, d, dtype=act, device=dev)
+        self.dgu = torch.empty(R, 2 * f, dtype=act, device=dev)
+        self.dx_perm = torch.empty(R, d, dtype=act, device=dev)
+        self.dx = torch.empty(self.T, d, dtype=act, device=dev)
+        self.dw13 = torch.empty(E, 2 * f, d, dtype=act, device=dev)
+        self.dw2 = torch.empty(E, d, f, dtype=act, device=dev)
+        self._bwd_alloc = True
+
+    # -------------------------------------------------------------- weights
+    def set_weights(self, w13, w2):
+        """Weights [E, 2f, d] and [E, d, f] (fp32 or bf16).  For MXFP8 the forward
+        and backward MXFP8 caches are made here (once per optimizer step)."""
+        self.w13, self.w2 = w13, w2
+        if self.dtype != MOE_MXFP8:
+            return
+        E, f, d = self.E, self.f, self.d
+        dev = self.device
+        u8 = dict(dtype=torch.uint8, device=dev)
+        # forward direction: blocks along the contraction dim of each GEMM
+        self.w13_q = torch.empty(E * 2 * f, d, **u8)
+        self.w13_s = torch.empty(E * 2 * f, d // 32, **u8)
+        moe_quantize_mxfp8(w13.reshape(E * 2 * f, d), 0, self.w13_q, self.w13_s)
+        self.w2_q = torch.empty(E * d, f, **u8)
+        self.w2_s = torch.empty(E * d, f // 32, **u8)
+        moe_quantize_mxfp8(w2.reshape(E * d, f), 0, self.w2_q, self.w2_s)
+        # backward direction: each expert's matrix transposed, blocks along 2f / d
+        g13 = torch.arange(0, E + 1, dtype=torch.int32, device=dev) * (2 * f)
+        g2 = torch.arange(0, E + 1, dtype=torch.int32, device=dev) * d
+        self.w13t_q = torch.empty(E * d * 2 * f, **u8)
+        self.w13t_s = torch.empty(E * d * 2 * f // 32, **u8)
+        moe_quantize_mxfp8(w13.reshape(E * 2 * f, d), 1, self.w13t_q, self.w13t_s, g13, E)
+        self.w2t_q = torch.empty(E * f * d, **u8)
+        self.w2t_s = torch.empty(E * f * d // 32, **u8)
+        moe_quantize_mxfp8(w2.reshape(E * d, f), 1, self.w2t_q, self.w2t_s, g2, E)
+
+    # -------------------------------------------------------------- steps
+    def route(self, logits):
+        moe_route_topk(logits, self.k, self.capacity, self.topk_idx, self.topk_w, self.counts,
+                       self.offsets, self.dst_row, self.src_slot, self.route_ws, self.dev_err)
+
+    def permute(self, x):
+        moe_permute(self.dtype, x, self.k, self.dst_row, self.x_perm, src_slot=self.src_slot,
+                    x_perm_scales=self.x_perm_scales, dev_err=self.dev_err)
+
+    def gemm_fwd(self):
+        if self.dtype == MOE_MXFP8:
+            moe_grouped_gemm_fwd(self.dtype, self.x_perm, self.w13_q, self.w2_q, self.offsets,
+                                 self.capacity, self.gu, self.h, self.y_perm,
+                                 x_perm_scales=self.x_perm_scales, w13_scales=self.w13_s,
+                                 w2_scales=self.w2_s, ws=self.gemm_ws)
+        else:
+            moe_grouped_gemm_fwd(self.dtype, self.x_perm, self.w13, self.w2, self.offsets,
+                                 self.capacity, self.gu, self.h, self.y_perm)
+
+    def combine(self, weights=None):
+        w = self.topk_w if weights is None else weights
+        moe_unpermute_combine(MOE_F32 if self.dtype == MOE_F32 else MOE_BF16, self.y_perm,
+                              self.dst_row, w, self.k, self.out, dev_err=self.dev_err)
+
+    def forward(self, logits, x, weights=None):
+        self.route(logits)
+        self.permute(x)
+        self.gemm_fwd()
+        self.combine(weights)
+        return self.out
+
+    def backward(self, dout, weights=None):
+        self._alloc_bwd()
+        act_dt = MOE_F32 if self.dtype == MOE_F32 else MOE_BF16
+        w = self.topk_w if weights is None else weights
+        moe_permute(act_dt, dout, self.k, self.dst_row, self.dy_perm, src_slot=self.src_slot,
+                    row_scale=w, dev_err=self.dev_err)
+        if self.dtype == MOE_MXFP8:
+            moe_grouped_gemm_bwd(self.dtype, self.dy_perm, self.x_perm, self.gu, self.h,
+                                 self.w13t_q, self.w2t_q, self.offsets, self.capacity, self.dgu,
+                                 self.dx_perm, self.dw13, self.dw2,
+                                 x_perm_scales=self.x_perm_scales, w13_scales=self.w13t_s,
+                                 w2_scales=self.w2t_s, ws=self.gemm_ws)
+        else:
+            moe_grouped_gemm_bwd(self.dtype, self.dy_perm, self.x_perm, self.gu, self.h,
+                                 self.w13, self.w2, self.offsets, self.capacity, self.dgu,
+                                 self.dx_perm, self.dw13, self.dw2)
+        moe_unpermute_combine(act_dt, self.dx_perm, self.dst_row, None, self.k, self.dx,
+                              dev_err=self.dev_err)
+        return self.dx, self.dw13, self.dw2

@@ -1,0 +1,60 @@
+"""Test helpers: the oracle's chain of the layer, and tensor comparison.
+
+Only the oracle is called here (never the HIP library); inputs come from
+moe_synth.  The oracle's outputs model the stored dtype of each tensor
+(round_mode), so they are comparable element by element with the GPU's.
+"""
+import numpy as np
+import torch
+
+import oracle
+
+BF16_TOL = 2e-2     # max|gpu - ref| <= BF16_TOL * max|ref|  (bf16 storage, fp32 accumulate)
+F32_TOL = 1e-4      # fp32 storage and accumulate, K <= a few thousand
+
+
+def np64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def oracle_layer(inp, k, capacity=0, round_mode=oracle.BF16, bwd=True, weights=None):
+    """Route, permute, grouped SwiGLU FFN, combine (and the backward) on the CPU."""
+    logits = inp["logits"].detach().cpu().numpy()
+    T = logits.shape[0]
+    r = oracle.route(logits, k, capacity)
+    go = oracle.group_offsets(r["offsets"], capacity)
+    w = r["topk_w"] if weights is None else np.asarray(weights, np.float32).reshape(T, k)
+    x, w13, w2 = np64(inp["x"]), np64(inp["w13"]), np64(inp["w2"])
+    xp = oracle.permute(x, r["dst_row"], k, r["n_rows"])
+    gu, h, y = oracle.ffn_fwd(xp, w13, w2, go, round_mode)
+    out = oracle.combine(y, r["dst_row"], w, T, k, round_mode)
+    res = dict(route=r, go=go, x_perm=xp, gu=gu, h=h, y_perm=y, out=out, w=w)
+    if bwd:
+        dout = np64(inp["dout"])
+        dy = oracle.permute(dout, r["dst_row"], k, r["n_rows"], row_scale=w, round_mode=round_mode)
+        dgu, dxp, dw13, dw2 = oracle.ffn_bwd(dy, xp, gu, h, w13, w2, go, round_mode)
+        dx = oracle.combine(dxp, r["dst_row"], None, T, k, round_mode)
+        res.update(dy_perm=dy, dgu=dgu, dx_perm=dxp, dw13=dw13, dw2=dw2, dx=dx)
+    return res
+
+
+def rel_err(gpu, ref):
+    """max|gpu - ref| / max|ref| (0 for empty tensors)."""
+    g = np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    if r.size == 0:
+        return 0.0
+    scale = np.abs(r).max()
+    err = np.abs(g - r).max()
+    if scale == 0:
+        return float(err)
+    return float(err / scale)
+
+
+def assert_close(gpu, ref, tol, name=""):
+    g = np.asarray(gpu, np.float64)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+    e = rel_err(g, ref)
+    assert e <= tol, f"{name}: max|gpu-ref|/max|ref| = {e:.3e} > {tol:.1e}"
+    return e

@@ -1,0 +1,142 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/moe.h declares, and rejects bad arguments on the
+host before anything is enqueued.  Every call below fails validation, so no
+kernel is ever launched from these tests.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import routing_grouped_gemm_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        pytest.skip("libmoe.so not built")
+    return m
+
+
+def _declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"MOE_API\s+[\w\s\*]*?\b(moe_\w+)\s*\(", text))
+
+
+def test_header_declares_the_abi(m):
+    assert _declared() == set(m.ABI_FUNCTIONS)
+
+
+def test_library_exports_every_declared_symbol(m):
+    out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert _declared() <= exported
+    lib = m.load()
+    for name in _declared():
+        assert hasattr(lib, name)
+
+
+def test_header_compiles_as_c():
+    src = '#include "moe.h"\nint main(void){return moe_version() > 0 ? 0 : 1;}\n'
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only",
+                        "-I" + os.path.dirname(HEADER), "-x", "c", "-"], input=src,
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_version_and_status_strings(m):
+    assert m.moe_version() >= 100
+    for st in (m.MOE_OK, m.MOE_EINVAL, m.MOE_EALIGN, m.MOE_EUNSUPPORTED, m.MOE_EWORKSPACE,
+               m.MOE_EHIP):
+        assert m.moe_status_string(st).startswith("MOE_")
+    assert "unknown" in m.moe_status_string(12345)
+
+
+def test_route_workspace_formula(m):
+    assert m.moe_route_workspace_bytes(-1, 8, 2) == 0
+    a = m.moe_route_workspace_bytes(16384, 128, 4)
+    # lrank (T*k int32) + one histogram row of E int32 per 64 tokens, plus alignment slack
+    assert a >= 16384 * 4 * 4 + 256 * 128 * 4
+    assert a < 16384 * 4 * 4 + 256 * 128 * 4 + 1024
+    assert m.moe_gemm_workspace_bytes(m.MOE_BF16, 8, 1000, 128, 128) == 0
+
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced (validation fails first)
+
+
+def test_route_argument_validation(m):
+    lib = m.load()
+    P = FAKE
+    ws = m.moe_route_workspace_bytes(100, 8, 2)
+
+    def call(T=100, E=8, k=2, C=0, n_rows=200, wsb=ws, logits=P, counts=P, src=P):
+        return lib.moe_route_topk(logits, T, E, k, C, P, P, counts, P, P, src, n_rows, P, wsb,
+                                  None, None)
+    assert call(k=9) == m.MOE_EINVAL                # k > 8
+    assert call(E=4, k=5) == m.MOE_EINVAL           # k > E
+    assert call(E=1025) == m.MOE_EINVAL             # too many experts
+    assert call(T=-1) == m.MOE_EINVAL
+    assert call(n_rows=199) == m.MOE_EINVAL         # n_rows != T*k
+    assert call(C=30, n_rows=200) == m.MOE_EINVAL   # padded: n_rows must be E*C
+    assert call(logits=None) == m.MOE_EINVAL
+    assert call(counts=None) == m.MOE_EINVAL
+    assert call(src=None) == m.MOE_EINVAL
+    assert call(wsb=ws - 1) == m.MOE_EWORKSPACE
+    assert call(C=-1) == m.MOE_EINVAL
+
+
+def test_permute_and_combine_validation(m):
+    lib = m.load()
+    P = FAKE
+    assert lib.moe_permute(9, P, 10, 64, 2, P, None, None, 20, P, None, None, None) == \
+        m.MOE_EUNSUPPORTED
+    assert lib.moe_permute(m.MOE_BF16, P, 10, 60, 2, P, None, None, 20, P, None, None, None) == \
+        m.MOE_EALIGN                                # d % 8
+    assert lib.moe_permute(m.MOE_BF16, P + 8, 10, 64, 2, P, None, None, 20, P, None, None,
+                           None) == m.MOE_EALIGN     # pointer alignment
+    assert lib.moe_permute(m.MOE_BF16, P, 10, 64, 2, P, None, None, 24, P, None, None, None) == \
+        m.MOE_EINVAL                                # padded layout needs src_slot
+    assert lib.moe_permute(m.MOE_MXFP8, P, 10, 64, 2, P, None, P, 20, P, P, None, None) == \
+        m.MOE_EUNSUPPORTED                          # no row scale with MXFP8
+    assert lib.moe_permute(m.MOE_MXFP8, P, 10, 48, 2, P, None, None, 20, P, P, None, None) == \
+        m.MOE_EALIGN                                # d % 32 for MXFP8
+    assert lib.moe_permute(m.MOE_BF16, P, 10, 64, 9, P, None, None, 90, P, None, None, None) == \
+        m.MOE_EINVAL                                # k > 8
+    assert lib.moe_unpermute_combine(m.MOE_MXFP8, P, P, None, 10, 2, 64, 20, P, None, None) == \
+        m.MOE_EUNSUPPORTED
+    assert lib.moe_unpermute_combine(m.MOE_BF16, P, None, None, 10, 2, 64, 20, P, None, None) == \
+        m.MOE_EINVAL
+    assert lib.moe_unpermute_combine(m.MOE_F32, P, P, None, 10, 2, 66, 20, P, None, None) == \
+        m.MOE_EALIGN
+
+
+def test_gemm_validation(m):
+    lib = m.load()
+    P = FAKE
+
+    def fwd(dtype=m.MOE_BF16, goff=P, C=0, E=8, n_rows=100, d=128, f=128, w13=P, ws=None,
+            wsb=0, xs=None):
+        return lib.moe_grouped_gemm_fwd(dtype, P, xs, w13, xs, P, xs, goff, C, E, n_rows, d, f,
+                                        P, P, P, ws, wsb, None)
+    assert fwd(dtype=5) == m.MOE_EUNSUPPORTED
+    assert fwd(goff=None) == m.MOE_EINVAL           # unpadded needs group offsets
+    assert fwd(C=10, n_rows=100, goff=None) == m.MOE_EINVAL   # E*C != n_rows
+    assert fwd(E=0) == m.MOE_EINVAL
+    assert fwd(E=2000) == m.MOE_EINVAL
+    assert fwd(d=100) == m.MOE_EALIGN
+    assert fwd(f=12) == m.MOE_EALIGN
+    assert fwd(w13=None) == m.MOE_EINVAL
+    assert fwd(w13=P + 2) == m.MOE_EALIGN
+    assert fwd(dtype=m.MOE_MXFP8, d=128, f=80) == m.MOE_EALIGN
+    assert fwd(dtype=m.MOE_MXFP8, xs=None) == m.MOE_EINVAL    # scales required
+    assert fwd(dtype=m.MOE_MXFP8, xs=P, ws=None) == m.MOE_EWORKSPACE
+    assert lib.moe_grouped_gemm_bwd(m.MOE_BF16, P, P, None, P, P, P, None, P, None, P, 0, 8, 100,
+                                    128, 128, P, P, None, P, None, 0, None) == m.MOE_EINVAL
+    assert lib.moe_quantize_mxfp8(P, 10, 48, 0, None, 0, P, P, None) == m.MOE_EALIGN
+    assert lib.moe_quantize_mxfp8(P, -1, 64, 0, None, 0, P, P, None) == m.MOE_EINVAL
+    assert lib.moe_quantize_mxfp8(P, 10, 64, 1, P, 0, P, P, None) == m.MOE_EINVAL

@@ -1,0 +1,190 @@
+"""GPU parity of the HIP path against the CPU oracle at sizes the oracle runs in
+seconds (several tiles per dimension, ragged tails, empty experts, ties).
+
+Integer outputs (top-k indices, counts, offsets, dst_row, src_slot, permuted
+bytes) must match bit for bit; topk_w within 1e-6; bf16 tensors within
+max|gpu - ref| <= 2e-2 * max|ref| (fp32 tensors 1e-4).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+from tests._chain import BF16_TOL, F32_TOL, assert_close, np64, oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import routing_grouped_gemm_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    m.load()
+    return m
+
+
+def _gpu_route(m, logits, k, capacity=0):
+    from routing_grouped_gemm_amd.layer import MoELayer
+    T, E = logits.shape
+    lay = MoELayer(T, 8, E, 8, k, m.MOE_BF16, capacity=capacity)
+    lay.route(logits.to(DEV))
+    torch.cuda.synchronize()
+    return lay
+
+
+def _check_route(lay, ref):
+    np.testing.assert_array_equal(lay.topk_idx.cpu().numpy(), ref["topk_idx"])
+    np.testing.assert_array_equal(lay.counts.cpu().numpy(), ref["counts"])
+    np.testing.assert_array_equal(lay.offsets.cpu().numpy(), ref["offsets"])
+    np.testing.assert_array_equal(lay.dst_row.cpu().numpy(), ref["dst_row"])
+    np.testing.assert_array_equal(lay.src_slot.cpu().numpy(), ref["src_slot"])
+    np.testing.assert_allclose(lay.topk_w.cpu().numpy(), ref["topk_w"], rtol=0, atol=1e-6)
+
+
+ROUTE_CASES = [(300, 6, 2), (1000, 128, 4), (513, 8, 8), (777, 1024, 3), (64, 16, 1),
+               (4097, 64, 4), (129, 256, 5), (65, 600, 8), (16384, 128, 4)]
+
+
+@pytest.mark.parametrize("T,E,k", ROUTE_CASES)
+def test_route_bit_exact(moe, T, E, k):
+    _say("route", T, E, k)
+    logits = moe_synth.normal((T, E), 1.0, seed=T * 7 + E)
+    lay = _gpu_route(moe, logits, k)
+    _check_route(lay, oracle.route(logits.numpy(), k))
+    assert int(lay.dev_err.item()) == 0
+
+
+@pytest.mark.parametrize("T,E,k", [(500, 8, 2), (300, 128, 4), (200, 1000, 8)])
+def test_route_ties_lowest_index(moe, T, E, k):
+    _say("route-ties", T, E, k)
+    g = torch.Generator().manual_seed(E)
+    logits = torch.randint(-2, 3, (T, E), generator=g).float()
+    logits[::7] = 0.0
+    logits[1::7, :] = -0.0
+    lay = _gpu_route(moe, logits, k)
+    _check_route(lay, oracle.route(logits.numpy(), k))
+
+
+@pytest.mark.parametrize("T,E,k,C", [(400, 8, 2, 90), (1000, 16, 4, 300), (256, 8, 2, 200)])
+def test_route_padded(moe, T, E, k, C):
+    _say("route-padded", T, E, k, C)
+    logits = moe_synth.router_logits(T, E, seed=C, routing="zipf")
+    lay = _gpu_route(moe, logits, k, capacity=C)
+    _check_route(lay, oracle.route(logits.numpy(), k, capacity=C))
+
+
+def test_route_empty_and_nonfinite(moe):
+    _say("route-empty")
+    lay = _gpu_route(moe, torch.zeros(0, 8), 2)
+    assert lay.counts.cpu().sum() == 0 and np.all(lay.offsets.cpu().numpy() == 0)
+    _say("route-nonfinite")
+    logits = moe_synth.normal((100, 8), 1.0, seed=3)
+    logits[5, 2] = float("nan")
+    logits[9, 0] = float("inf")
+    lay = _gpu_route(moe, logits, 2)
+    assert int(lay.dev_err.item()) & moe.MOE_ERR_NONFINITE_LOGIT
+    ok = np.ones(100, bool)
+    ok[[5, 9]] = False
+    ref = oracle.route(logits.nan_to_num(nan=-np.inf, posinf=-np.inf).numpy().clip(min=-3e38), 2)
+    np.testing.assert_array_equal(lay.topk_idx.cpu().numpy()[ok], ref["topk_idx"][ok])
+
+
+def test_route_deterministic(moe):
+    _say("route-determinism")
+    logits = moe_synth.normal((5000, 128), 1.0, seed=77)
+    a = _gpu_route(moe, logits, 4)
+    b = _gpu_route(moe, logits, 4)
+    for name in ("topk_idx", "topk_w", "dst_row", "src_slot", "offsets"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+
+
+# ------------------------------------------------------------------ layer
+LAYER_CASES = [
+    # T, d, E, f, k, dtype, capacity
+    (384, 256, 5, 384, 2, "bf16", 0),
+    (200, 200, 7, 136, 3, "bf16", 0),
+    (512, 128, 8, 256, 2, "bf16", 0),
+    (300, 64, 1, 64, 1, "bf16", 0),
+    (256, 128, 16, 64, 8, "bf16", 0),
+    (400, 128, 8, 128, 2, "bf16", 70),
+    (256, 128, 8, 256, 2, "f32", 0),
+    (130, 72, 3, 40, 2, "f32", 0),
+]
+
+
+def _run_layer(m, inp, k, dtype, capacity, empty_expert=None):
+    from routing_grouped_gemm_amd.layer import MoELayer
+    T, d = inp["x"].shape
+    E, two_f, _ = inp["w13"].shape
+    dt = m.MOE_F32 if dtype == "f32" else m.MOE_BF16
+    lay = MoELayer(T, d, E, two_f // 2, k, dt, capacity=capacity)
+    g = {n: inp[n].to(DEV) for n in ("logits", "x", "w13", "w2", "dout")}
+    lay.set_weights(g["w13"], g["w2"])
+    lay.forward(g["logits"], g["x"])
+    lay.backward(g["dout"])
+    torch.cuda.synchronize()
+    return lay
+
+
+@pytest.mark.parametrize("T,d,E,f,k,dtype,C", LAYER_CASES)
+def test_layer_fwd_bwd_parity(moe, T, d, E, f, k, dtype, C):
+    _say("layer", T, d, E, f, k, dtype, C)
+    inp = moe_synth.make_inputs(T=T, d=d, E=E, f=f, k=k, dtype=dtype, seed=T + d + E + f + k)
+    if E > 2:
+        inp["logits"][:, E - 2] -= 1e30            # one expert gets no rows
+    lay = _run_layer(moe, inp, k, dtype, C)
+    rm = oracle.FP32 if dtype == "f32" else oracle.BF16
+    tol = F32_TOL if dtype == "f32" else BF16_TOL
+    ref = oracle_layer(inp, k, capacity=C, round_mode=rm)
+    _check_route(lay, ref["route"])
+    assert int(lay.dev_err.item()) == 0
+    # permute is a byte copy of the token rows (padding rows zero)
+    np.testing.assert_array_equal(np64(lay.x_perm), ref["x_perm"])
+    rows = ref["route"]["src_slot"] >= 0
+    assert_close(np64(lay.gu)[rows], ref["gu"][rows], tol, "gu")
+    assert_close(np64(lay.h)[rows], ref["h"][rows], tol, "h")
+    assert_close(np64(lay.y_perm)[rows], ref["y_perm"][rows], tol, "y_perm")
+    assert_close(np64(lay.out), ref["out"], tol, "out")
+    assert_close(np64(lay.dy_perm)[rows], ref["dy_perm"][rows], tol, "dy_perm")
+    assert_close(np64(lay.dgu)[rows], ref["dgu"][rows], tol, "dgu")
+    assert_close(np64(lay.dx_perm)[rows], ref["dx_perm"][rows], tol, "dx_perm")
+    assert_close(np64(lay.dx), ref["dx"], tol, "dx")
+    assert_close(np64(lay.dw13), ref["dw13"], tol, "dw13")
+    assert_close(np64(lay.dw2), ref["dw2"], tol, "dw2")
+    if E > 2:
+        assert torch.all(lay.dw13[E - 2] == 0) and torch.all(lay.dw2[E - 2] == 0)
+
+
+def test_layer_deterministic(moe):
+    _say("layer-determinism")
+    inp = moe_synth.make_inputs(T=384, d=256, E=5, f=384, k=2, seed=5)
+    a = _run_layer(moe, inp, 2, "bf16", 0)
+    b = _run_layer(moe, inp, 2, "bf16", 0)
+    for name in ("gu", "h", "y_perm", "out", "dgu", "dx_perm", "dx", "dw13", "dw2"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+
+
+def test_permute_row_range_error_is_flagged(moe):
+    _say("permute-row-range")
+    T, d, k = 16, 64, 2
+    x = torch.randn(T, d, device=DEV).to(torch.bfloat16)
+    dst = torch.arange(T * k, dtype=torch.int32, device=DEV)
+    dst[5] = T * k + 3                                  # outside x_perm
+    xp = torch.zeros(T * k, d, dtype=torch.bfloat16, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    moe.moe_permute(moe.MOE_BF16, x, k, dst, xp, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & moe.MOE_ERR_ROW_RANGE
+    ok = torch.ones(T * k, dtype=torch.bool)
+    ok[5] = False
+    assert torch.equal(xp.cpu()[ok], x.cpu().repeat_interleave(k, 0)[ok])
