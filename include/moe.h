@@ -190,6 +190,45 @@ MOE_API int moe_grouped_gemm_bwd(int dtype, const void* dy_perm, const void* x_p
                          int d, int f, void* dgu, void* dx_perm, void* dw13, void* dw2,
                          void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* The grouped GEMM stages, one kernel launch each (MOE_F32 / MOE_BF16). */
+enum moe_gemm_op {
+    MOE_GEMM_GATE_UP = 0,        /* gu = x [Wg | Wu]^T, h = silu(g) * u               */
+    MOE_GEMM_DOWN = 1,           /* y = h Wd^T                                        */
+    MOE_GEMM_DGRAD_DOWN = 2,     /* dh = dy Wd; dgu = [dg | du] from dh and saved gu  */
+    MOE_GEMM_DGRAD_GATE_UP = 3,  /* dx = dg Wg + du Wu                                */
+    MOE_GEMM_WGRAD = 4           /* dWd = sum dy^T h and dWg|dWu = sum dgu^T x        */
+};
+
+/* Operands of the grouped GEMM stages (device pointers; unused ones may be
+ * NULL).  Shapes and layouts as in moe_grouped_gemm_fwd / _bwd. */
+typedef struct moe_gemm_tensors {
+    const void* x_perm;          /* [n_rows, d]                     */
+    const uint8_t* x_perm_scales;
+    const void* w13;             /* [E, 2f, d]                      */
+    const uint8_t* w13_scales;
+    const void* w2;              /* [E, d, f]                       */
+    const uint8_t* w2_scales;
+    void* gu;                    /* [n_rows, 2f]                    */
+    void* h;                     /* [n_rows, f]                     */
+    void* y_perm;                /* [n_rows, d]                     */
+    const void* dy_perm;         /* [n_rows, d]                     */
+    void* dgu;                   /* [n_rows, 2f]                    */
+    void* dx_perm;               /* [n_rows, d]                     */
+    void* dw13;                  /* [E, 2f, d]                      */
+    void* dw2;                   /* [E, d, f]                       */
+} moe_gemm_tensors;
+
+/*
+ * One stage of the grouped SwiGLU GEMM (the forward and backward calls above
+ * are GATE_UP + DOWN and DGRAD_DOWN + DGRAD_GATE_UP + WGRAD).  Exactly one
+ * kernel launch for MOE_F32 and MOE_BF16; MOE_MXFP8 returns
+ * MOE_EUNSUPPORTED (use the fwd / bwd calls).  Inputs a stage reads must have
+ * been produced by the earlier stages on the same stream.
+ */
+MOE_API int moe_grouped_gemm_op(int op, int dtype, const moe_gemm_tensors* t,
+                                const int32_t* group_off, int capacity, int E, int64_t n_rows,
+                                int d, int f, moe_stream_t stream);
+
 /*
  * Un-permute and combine (tutorial, "rowwise EP": the reverse transfer and
  * the merge of each token's k expert outputs):

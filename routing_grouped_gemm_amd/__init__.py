@@ -18,10 +18,21 @@ MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, 
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
 MOE_ERR_NONFINITE_LOGIT, MOE_ERR_ROW_RANGE = 1, 2
 
+MOE_GEMM_GATE_UP, MOE_GEMM_DOWN, MOE_GEMM_DGRAD_DOWN, MOE_GEMM_DGRAD_GATE_UP, MOE_GEMM_WGRAD = \
+    0, 1, 2, 3, 4
+
 ABI_FUNCTIONS = ("moe_route_workspace_bytes", "moe_route_topk", "moe_permute",
                  "moe_gemm_workspace_bytes", "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd",
-                 "moe_unpermute_combine", "moe_quantize_mxfp8", "moe_status_string",
-                 "moe_version")
+                 "moe_grouped_gemm_op", "moe_unpermute_combine", "moe_quantize_mxfp8",
+                 "moe_status_string", "moe_version")
+
+GEMM_TENSOR_FIELDS = ("x_perm", "x_perm_scales", "w13", "w13_scales", "w2", "w2_scales", "gu",
+                      "h", "y_perm", "dy_perm", "dgu", "dx_perm", "dw13", "dw2")
+
+
+class MoeGemmTensors(ctypes.Structure):
+    """C struct moe_gemm_tensors (device pointers, NULL where unused)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in GEMM_TENSOR_FIELDS]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
@@ -62,6 +73,9 @@ def load():
     lib.moe_grouped_gemm_bwd.restype = I
     lib.moe_grouped_gemm_bwd.argtypes = [I, P, P, P, P, P, P, P, P, P, P, I, I, I64, I, I, P, P, P,
                                          P, P, SZ, P]
+    lib.moe_grouped_gemm_op.restype = I
+    lib.moe_grouped_gemm_op.argtypes = [I, I, ctypes.POINTER(MoeGemmTensors), P, I, I, I64, I, I,
+                                        P]
     lib.moe_unpermute_combine.restype = I
     lib.moe_unpermute_combine.argtypes = [I, P, P, P, I, I, I, I64, P, P, P]
     lib.moe_quantize_mxfp8.restype = I
@@ -164,6 +178,21 @@ def moe_grouped_gemm_bwd(dtype, dy_perm, x_perm, gu, h, w13, w2, group_off, capa
                                      _p(dx_perm), _p(dw13), _p(dw2), _p(ws), _nbytes(ws),
                                      _s(stream))
     _check(rc, "moe_grouped_gemm_bwd")
+
+
+def gemm_tensors(**tensors):
+    """Build a MoeGemmTensors from keyword tensors (names as in GEMM_TENSOR_FIELDS)."""
+    bad = set(tensors) - set(GEMM_TENSOR_FIELDS)
+    if bad:
+        raise TypeError(f"unknown operand(s) {sorted(bad)}")
+    return MoeGemmTensors(**{n: _p(t) for n, t in tensors.items()})
+
+
+def moe_grouped_gemm_op(op, dtype, tensors, group_off, capacity, E, n_rows, d, f, stream=None):
+    """One grouped GEMM stage (one kernel launch); tensors is a MoeGemmTensors."""
+    rc = load().moe_grouped_gemm_op(op, dtype, ctypes.byref(tensors), _p(group_off), capacity, E,
+                                    n_rows, d, f, _s(stream))
+    _check(rc, "moe_grouped_gemm_op")
 
 
 def moe_unpermute_combine(dtype, y_perm, dst_row, weights, k, out, dev_err=None, stream=None):

@@ -142,8 +142,9 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb, f
                                          uint16_t* smem)
 {
     constexpr int MI = BM / 64;
-    uint16_t* sA[2] = {smem, smem + (BM + BN) * LDT};
-    uint16_t* sB[2] = {smem + BM * LDT, smem + (BM + BN) * LDT + BM * LDT};
+    // stage s: A tile at smem + s * STAGE, B tile right after it.  Offsets (not
+    // a table of pointers) keep every access in the LDS address space.
+    constexpr int STAGE = (BM + BN) * LDT;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -163,8 +164,8 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb, f
     Loader<BN, B_MN> lb;
     la.load(sa, 0);
     lb.load(sb, 0);
-    la.store(sA[0]);
-    lb.store(sB[0]);
+    la.store(smem);
+    lb.store(smem + BM * LDT);
     __syncthreads();
 
     const int arow = wm * (BM / 2) + (lane & 31);
@@ -176,8 +177,8 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb, f
             la.load(sa, (kt + 1) * BK);
             lb.load(sb, (kt + 1) * BK);
         }
-        const uint16_t* a_s = sA[cur];
-        const uint16_t* b_s = sB[cur];
+        const uint16_t* a_s = smem + cur * STAGE;
+        const uint16_t* b_s = a_s + BM * LDT;
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             bf16x8 af[MI], bfr[4];
@@ -196,8 +197,9 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb, f
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
         if (more) {
-            la.store(sA[cur ^ 1]);
-            lb.store(sB[cur ^ 1]);
+            uint16_t* nxt = smem + (cur ^ 1) * STAGE;
+            la.store(nxt);
+            lb.store(nxt + BM * LDT);
         }
         __syncthreads();
     }
@@ -338,26 +340,34 @@ __global__ __launch_bounds__(NTH, 1) void gemm_grouped_m_kernel(MParams p)
     epilogue_m<BM, EPI>(acc, p, row0, rows_valid, nt);
 }
 
-struct KParams {
+struct KProblem {
     const uint16_t* A;     // [n_rows, M] (M contiguous); group e's rows are its K
     int64_t lda;
     const uint16_t* B;     // [n_rows, N] (N contiguous)
     int64_t ldb;
     int M, N;
-    const int32_t* group_off;
-    int capacity, E;
-    int64_t n_rows;
     int mtn, ntn;
     uint16_t* C;           // [E, M, N]
     int64_t ldc, sC;
 };
 
-// Grouped-K GEMM (weight gradient): C_e = A_e^T B_e over the rows of group e.
+struct KParams {
+    KProblem pr[2];        // up to two weight gradients in one launch
+    int nprob;
+    const int32_t* group_off;
+    int capacity, E;
+    int64_t n_rows;
+};
+
+// Grouped-K GEMM (weight gradients): C_e = A_e^T B_e over the rows of group e,
+// for one or two problems sharing the groups.  Tiles are expert-major so the
+// tiles reading one expert's rows run together on one XCD.
 template <int BM>
 __global__ __launch_bounds__(NTH, 1) void gemm_grouped_k_kernel(KParams p)
 {
     __shared__ __align__(16) uint16_t smem[2 * (BM + BN) * LDT];
-    const int tiles_e = p.mtn * p.ntn;
+    const int t0 = p.pr[0].mtn * p.pr[0].ntn;
+    const int tiles_e = t0 + (p.nprob > 1 ? p.pr[1].mtn * p.pr[1].ntn : 0);
     const int total = p.E * tiles_e;
     const int per_xcd = (total + 7) / 8;
     const int xcd = blockIdx.x % 8;
@@ -366,22 +376,25 @@ __global__ __launch_bounds__(NTH, 1) void gemm_grouped_k_kernel(KParams p)
     const int L = xcd * per_xcd + slot;
     if (L >= total) return;
     const int e = L / tiles_e;
-    const int local = L - e * tiles_e;
-    const int mt = local / p.ntn;
-    const int nt = local - mt * p.ntn;
+    int local = L - e * tiles_e;
+    const int which = local < t0 ? 0 : 1;
+    if (which) local -= t0;
+    const KProblem& q = p.pr[which];
+    const int mt = local / q.ntn;
+    const int nt = local - mt * q.ntn;
     const int64_t g0 = group_begin(p.group_off, p.capacity, e, p.n_rows);
     const int m_e = (int)group_rows(p.group_off, p.capacity, e, p.n_rows);
 
     TileSrc sa;
-    sa.p0 = sa.p1 = p.A + g0 * p.lda + (int64_t)mt * BM;
-    sa.ld = p.lda;
-    sa.rows0 = min(BM, p.M - mt * BM);
+    sa.p0 = sa.p1 = q.A + g0 * q.lda + (int64_t)mt * BM;
+    sa.ld = q.lda;
+    sa.rows0 = min(BM, q.M - mt * BM);
     sa.rows1 = 0;
     sa.K = m_e;
     TileSrc sb;
-    sb.p0 = sb.p1 = p.B + g0 * p.ldb + (int64_t)nt * BN;
-    sb.ld = p.ldb;
-    sb.rows0 = min(BN, p.N - nt * BN);
+    sb.p0 = sb.p1 = q.B + g0 * q.ldb + (int64_t)nt * BN;
+    sb.ld = q.ldb;
+    sb.rows0 = min(BN, q.N - nt * BN);
     sb.rows1 = 0;
     sb.K = m_e;
 
@@ -394,17 +407,17 @@ __global__ __launch_bounds__(NTH, 1) void gemm_grouped_k_kernel(KParams p)
     const int lane = tid & 63;
     const int wm = wave >> 1;
     const int wn = wave & 1;
-    uint16_t* Ce = p.C + (int64_t)e * p.sC;
+    uint16_t* Ce = q.C + (int64_t)e * q.sC;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int m = mt * BM + wm * (BM / 2) + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            if (m >= p.M) continue;
+            if (m >= q.M) continue;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int n = nt * BN + tile_col(wn, j, lane);
-                if (n < p.N) Ce[(int64_t)m * p.ldc + n] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+                if (n < q.N) Ce[(int64_t)m * q.ldc + n] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
             }
         }
 }
@@ -424,7 +437,9 @@ hipError_t launch_m(const MParams& p, int64_t n_rows, hipStream_t s)
 template <int BM>
 hipError_t launch_k(const KParams& p, hipStream_t s)
 {
-    const int64_t total = (int64_t)p.E * p.mtn * p.ntn;
+    int64_t tiles_e = 0;
+    for (int i = 0; i < p.nprob; ++i) tiles_e += (int64_t)p.pr[i].mtn * p.pr[i].ntn;
+    const int64_t total = (int64_t)p.E * tiles_e;
     const int64_t grid = (total + 7) / 8 * 8;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((gemm_grouped_k_kernel<BM>), dim3((unsigned)grid), dim3(NTH), 0, s, p);
@@ -435,129 +450,104 @@ constexpr int kBM = 128;
 
 }  // namespace
 
-hipError_t gemm_fwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, GroupSpec g,
-                         int d, int f, uint16_t* gu, uint16_t* h, uint16_t* y, hipStream_t s)
+hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, int f,
+                        hipStream_t s)
 {
     MParams p{};
     p.group_off = g.group_off;
     p.capacity = g.capacity;
     p.E = g.E;
     p.n_rows = g.n_rows;
-    // gate/up with the SwiGLU epilogue: gu = x [Wg|Wu]^T, h = silu(g) * u
-    p.A = x;
-    p.lda = d;
-    p.B = w13;
-    p.ldb = d;
-    p.sB = (int64_t)2 * f * d;
-    p.N = f;
-    p.K = d;
-    p.ntn = (f + 127) / 128;
-    p.C = gu;
-    p.ldc = 2 * f;
-    p.H = h;
-    p.ldh = f;
     p.f = f;
-    hipError_t err = launch_m<kBM, false, EPI_SWIGLU_FWD>(p, g.n_rows, s);
-    if (err != hipSuccess) return err;
-    // down: y = h Wd^T
-    MParams q{};
-    q.group_off = g.group_off;
-    q.capacity = g.capacity;
-    q.E = g.E;
-    q.n_rows = g.n_rows;
-    q.A = h;
-    q.lda = f;
-    q.B = w2;
-    q.ldb = f;
-    q.sB = (int64_t)d * f;
-    q.N = d;
-    q.K = f;
-    q.ntn = (d + BN - 1) / BN;
-    q.C = y;
-    q.ldc = d;
-    return launch_m<kBM, false, EPI_STORE>(q, g.n_rows, s);
-}
-
-hipError_t gemm_bwd_bf16(const uint16_t* dy, const uint16_t* x, const uint16_t* gu,
-                         const uint16_t* h, const uint16_t* w13, const uint16_t* w2, GroupSpec g,
-                         int d, int f, uint16_t* dgu, uint16_t* dx, uint16_t* dw13,
-                         uint16_t* dw2, hipStream_t s)
-{
-    // dgrad 1: dh = dy Wd (Wd_e stored [d, f] = [K, N]) with the SwiGLU backward
-    MParams p{};
-    p.group_off = g.group_off;
-    p.capacity = g.capacity;
-    p.E = g.E;
-    p.n_rows = g.n_rows;
-    p.A = dy;
-    p.lda = d;
-    p.B = w2;
-    p.ldb = f;
-    p.sB = (int64_t)d * f;
-    p.N = f;
-    p.K = d;
-    p.ntn = (f + BN - 1) / BN;
-    p.C = dgu;
-    p.ldc = 2 * f;
-    p.G = gu;
-    p.ldg = 2 * f;
-    p.f = f;
-    hipError_t err = launch_m<kBM, true, EPI_SWIGLU_BWD>(p, g.n_rows, s);
-    if (err != hipSuccess) return err;
-    // dgrad 2: dx = [dg | du] [Wg ; Wu]  (W13_e stored [2f, d] = [K, N])
-    MParams q{};
-    q.group_off = g.group_off;
-    q.capacity = g.capacity;
-    q.E = g.E;
-    q.n_rows = g.n_rows;
-    q.A = dgu;
-    q.lda = 2 * f;
-    q.B = w13;
-    q.ldb = d;
-    q.sB = (int64_t)2 * f * d;
-    q.N = d;
-    q.K = 2 * f;
-    q.ntn = (d + BN - 1) / BN;
-    q.C = dx;
-    q.ldc = d;
-    err = launch_m<kBM, true, EPI_STORE>(q, g.n_rows, s);
-    if (err != hipSuccess) return err;
-    // wgrad: dWd_e [d, f] = dy_e^T h_e ; dW13_e [2f, d] = dgu_e^T x_e
-    KParams a{};
-    a.group_off = g.group_off;
-    a.capacity = g.capacity;
-    a.E = g.E;
-    a.n_rows = g.n_rows;
-    a.A = dy;
-    a.lda = d;
-    a.B = h;
-    a.ldb = f;
-    a.M = d;
-    a.N = f;
-    a.mtn = (d + kBM - 1) / kBM;
-    a.ntn = (f + BN - 1) / BN;
-    a.C = dw2;
-    a.ldc = f;
-    a.sC = (int64_t)d * f;
-    err = launch_k<kBM>(a, s);
-    if (err != hipSuccess) return err;
-    KParams b{};
-    b.group_off = g.group_off;
-    b.capacity = g.capacity;
-    b.E = g.E;
-    b.n_rows = g.n_rows;
-    b.A = dgu;
-    b.lda = 2 * f;
-    b.B = x;
-    b.ldb = d;
-    b.M = 2 * f;
-    b.N = d;
-    b.mtn = (2 * f + kBM - 1) / kBM;
-    b.ntn = (d + BN - 1) / BN;
-    b.C = dw13;
-    b.ldc = d;
-    b.sC = (int64_t)2 * f * d;
-    return launch_k<kBM>(b, s);
+    switch (op) {
+    case MOE_GEMM_GATE_UP:  // gu = x [Wg|Wu]^T, h = silu(g) * u
+        p.A = (const uint16_t*)t.x_perm;
+        p.lda = d;
+        p.B = (const uint16_t*)t.w13;
+        p.ldb = d;
+        p.sB = (int64_t)2 * f * d;
+        p.N = f;
+        p.K = d;
+        p.ntn = (f + 127) / 128;
+        p.C = (uint16_t*)t.gu;
+        p.ldc = 2 * f;
+        p.H = (uint16_t*)t.h;
+        p.ldh = f;
+        return launch_m<kBM, false, EPI_SWIGLU_FWD>(p, g.n_rows, s);
+    case MOE_GEMM_DOWN:  // y = h Wd^T
+        p.A = (const uint16_t*)t.h;
+        p.lda = f;
+        p.B = (const uint16_t*)t.w2;
+        p.ldb = f;
+        p.sB = (int64_t)d * f;
+        p.N = d;
+        p.K = f;
+        p.ntn = (d + BN - 1) / BN;
+        p.C = (uint16_t*)t.y_perm;
+        p.ldc = d;
+        return launch_m<kBM, false, EPI_STORE>(p, g.n_rows, s);
+    case MOE_GEMM_DGRAD_DOWN:  // dh = dy Wd (Wd_e stored [d, f] = [K, N]), SwiGLU backward
+        p.A = (const uint16_t*)t.dy_perm;
+        p.lda = d;
+        p.B = (const uint16_t*)t.w2;
+        p.ldb = f;
+        p.sB = (int64_t)d * f;
+        p.N = f;
+        p.K = d;
+        p.ntn = (f + BN - 1) / BN;
+        p.C = (uint16_t*)t.dgu;
+        p.ldc = 2 * f;
+        p.G = (const uint16_t*)t.gu;
+        p.ldg = 2 * f;
+        return launch_m<kBM, true, EPI_SWIGLU_BWD>(p, g.n_rows, s);
+    case MOE_GEMM_DGRAD_GATE_UP:  // dx = [dg | du] [Wg ; Wu] (W13_e stored [2f, d] = [K, N])
+        p.A = (const uint16_t*)t.dgu;
+        p.lda = 2 * f;
+        p.B = (const uint16_t*)t.w13;
+        p.ldb = d;
+        p.sB = (int64_t)2 * f * d;
+        p.N = d;
+        p.K = 2 * f;
+        p.ntn = (d + BN - 1) / BN;
+        p.C = (uint16_t*)t.dx_perm;
+        p.ldc = d;
+        return launch_m<kBM, true, EPI_STORE>(p, g.n_rows, s);
+    case MOE_GEMM_WGRAD: {  // dWd_e [d, f] = dy_e^T h_e ; dW13_e [2f, d] = dgu_e^T x_e
+        KParams k{};
+        k.group_off = g.group_off;
+        k.capacity = g.capacity;
+        k.E = g.E;
+        k.n_rows = g.n_rows;
+        k.nprob = 2;
+        KProblem& a = k.pr[0];
+        a.A = (const uint16_t*)t.dy_perm;
+        a.lda = d;
+        a.B = (const uint16_t*)t.h;
+        a.ldb = f;
+        a.M = d;
+        a.N = f;
+        a.mtn = (d + kBM - 1) / kBM;
+        a.ntn = (f + BN - 1) / BN;
+        a.C = (uint16_t*)t.dw2;
+        a.ldc = f;
+        a.sC = (int64_t)d * f;
+        KProblem& b = k.pr[1];
+        b.A = (const uint16_t*)t.dgu;
+        b.lda = 2 * f;
+        b.B = (const uint16_t*)t.x_perm;
+        b.ldb = d;
+        b.M = 2 * f;
+        b.N = d;
+        b.mtn = (2 * f + kBM - 1) / kBM;
+        b.ntn = (d + BN - 1) / BN;
+        b.C = (uint16_t*)t.dw13;
+        b.ldc = d;
+        b.sC = (int64_t)2 * f * d;
+        return launch_k<kBM>(k, s);
+    }
+    default:
+        return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace moe

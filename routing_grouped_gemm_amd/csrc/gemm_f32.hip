@@ -136,28 +136,37 @@ __global__ __launch_bounds__(256) void f32_grouped_m_kernel(F32M p)
     }
 }
 
-struct F32K {
+struct F32KProblem {
     const float* A;        // [n_rows, M]
     int64_t lda;
     const float* B;        // [n_rows, N]
     int64_t ldb;
-    int M, N;
-    const int32_t* group_off;
-    int capacity, E, mtn, ntn;
-    int64_t n_rows;
+    int M, N, mtn, ntn;
     float* C;              // [E, M, N]
     int64_t ldc, sC;
+};
+
+struct F32K {
+    F32KProblem pr[2];
+    int nprob;
+    const int32_t* group_off;
+    int capacity, E;
+    int64_t n_rows;
 };
 
 __global__ __launch_bounds__(256) void f32_grouped_k_kernel(F32K p)
 {
     __shared__ float sA[TK][TM + 4];
     __shared__ float sB[TK][TN + 4];
-    const int tiles_e = p.mtn * p.ntn;
+    const int t0 = p.pr[0].mtn * p.pr[0].ntn;
+    const int tiles_e = t0 + (p.nprob > 1 ? p.pr[1].mtn * p.pr[1].ntn : 0);
     const int L = blockIdx.x;
     const int e = L / tiles_e;
-    const int local = L - e * tiles_e;
-    const int mt = local / p.ntn, nt = local - (local / p.ntn) * p.ntn;
+    int local = L - e * tiles_e;
+    const int which = local < t0 ? 0 : 1;
+    if (which) local -= t0;
+    const F32KProblem& q = p.pr[which];
+    const int mt = local / q.ntn, nt = local - (local / q.ntn) * q.ntn;
     const int64_t g0 = group_begin(p.group_off, p.capacity, e, p.n_rows);
     const int m_e = (int)group_rows(p.group_off, p.capacity, e, p.n_rows);
     const int m0 = mt * TM, n0 = nt * TN;
@@ -168,8 +177,8 @@ __global__ __launch_bounds__(256) void f32_grouped_k_kernel(F32K p)
         for (int idx = tid; idx < TM * TK; idx += 256) {
             const int kk = idx / TM, c = idx % TM;
             const int k = k0 + kk;
-            sA[kk][c] = (k < m_e && m0 + c < p.M) ? p.A[(g0 + k) * p.lda + m0 + c] : 0.0f;
-            sB[kk][c] = (k < m_e && n0 + c < p.N) ? p.B[(g0 + k) * p.ldb + n0 + c] : 0.0f;
+            sA[kk][c] = (k < m_e && m0 + c < q.M) ? q.A[(g0 + k) * q.lda + m0 + c] : 0.0f;
+            sB[kk][c] = (k < m_e && n0 + c < q.N) ? q.B[(g0 + k) * q.ldb + n0 + c] : 0.0f;
         }
         __syncthreads();
 #pragma unroll
@@ -186,13 +195,13 @@ __global__ __launch_bounds__(256) void f32_grouped_k_kernel(F32K p)
         }
         __syncthreads();
     }
-    float* Ce = p.C + (int64_t)e * p.sC;
+    float* Ce = q.C + (int64_t)e * q.sC;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
-            if (m < p.M && n < p.N) Ce[(int64_t)m * p.ldc + n] = acc[i][j];
+            if (m < q.M && n < q.N) Ce[(int64_t)m * q.ldc + n] = acc[i][j];
         }
 }
 
@@ -206,134 +215,117 @@ hipError_t launch_m(const F32M& p, int64_t n_rows, hipStream_t s)
 
 hipError_t launch_k(const F32K& p, hipStream_t s)
 {
-    const int64_t grid = (int64_t)p.E * p.mtn * p.ntn;
+    int64_t tiles_e = 0;
+    for (int i = 0; i < p.nprob; ++i) tiles_e += (int64_t)p.pr[i].mtn * p.pr[i].ntn;
+    const int64_t grid = (int64_t)p.E * tiles_e;
     if (grid > 0) hipLaunchKernelGGL(f32_grouped_k_kernel, dim3((unsigned)grid), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t gemm_fwd_f32(const float* x, const float* w13, const float* w2, GroupSpec g, int d,
-                        int f, float* gu, float* h, float* y, hipStream_t s)
+hipError_t gemm_op_f32(int op, const moe_gemm_tensors& t, GroupSpec g, int d, int f,
+                       hipStream_t s)
 {
     F32M p{};
     p.group_off = g.group_off;
     p.capacity = g.capacity;
     p.E = g.E;
     p.n_rows = g.n_rows;
-    p.A = x;
-    p.lda = d;
-    p.B = w13;
-    p.ldb = d;
-    p.sB = (int64_t)2 * f * d;
-    p.b_mn = false;
-    p.N = f;
-    p.K = d;
-    p.ntn = (f + TN / 2 - 1) / (TN / 2);
-    p.C = gu;
-    p.ldc = 2 * f;
-    p.H = h;
-    p.ldh = f;
     p.f = f;
-    hipError_t err = launch_m<EPI_SWIGLU_FWD>(p, g.n_rows, s);
-    if (err != hipSuccess) return err;
-    F32M q{};
-    q.group_off = g.group_off;
-    q.capacity = g.capacity;
-    q.E = g.E;
-    q.n_rows = g.n_rows;
-    q.A = h;
-    q.lda = f;
-    q.B = w2;
-    q.ldb = f;
-    q.sB = (int64_t)d * f;
-    q.b_mn = false;
-    q.N = d;
-    q.K = f;
-    q.ntn = (d + TN - 1) / TN;
-    q.C = y;
-    q.ldc = d;
-    return launch_m<EPI_STORE>(q, g.n_rows, s);
-}
-
-hipError_t gemm_bwd_f32(const float* dy, const float* x, const float* gu, const float* h,
-                        const float* w13, const float* w2, GroupSpec g, int d, int f, float* dgu,
-                        float* dx, float* dw13, float* dw2, hipStream_t s)
-{
-    F32M p{};
-    p.group_off = g.group_off;
-    p.capacity = g.capacity;
-    p.E = g.E;
-    p.n_rows = g.n_rows;
-    p.A = dy;
-    p.lda = d;
-    p.B = w2;
-    p.ldb = f;
-    p.sB = (int64_t)d * f;
-    p.b_mn = true;
-    p.N = f;
-    p.K = d;
-    p.ntn = (f + TN - 1) / TN;
-    p.C = dgu;
-    p.ldc = 2 * f;
-    p.G = gu;
-    p.ldg = 2 * f;
-    p.f = f;
-    hipError_t err = launch_m<EPI_SWIGLU_BWD>(p, g.n_rows, s);
-    if (err != hipSuccess) return err;
-    F32M q{};
-    q.group_off = g.group_off;
-    q.capacity = g.capacity;
-    q.E = g.E;
-    q.n_rows = g.n_rows;
-    q.A = dgu;
-    q.lda = 2 * f;
-    q.B = w13;
-    q.ldb = d;
-    q.sB = (int64_t)2 * f * d;
-    q.b_mn = true;
-    q.N = d;
-    q.K = 2 * f;
-    q.ntn = (d + TN - 1) / TN;
-    q.C = dx;
-    q.ldc = d;
-    err = launch_m<EPI_STORE>(q, g.n_rows, s);
-    if (err != hipSuccess) return err;
-    F32K a{};
-    a.group_off = g.group_off;
-    a.capacity = g.capacity;
-    a.E = g.E;
-    a.n_rows = g.n_rows;
-    a.A = dy;
-    a.lda = d;
-    a.B = h;
-    a.ldb = f;
-    a.M = d;
-    a.N = f;
-    a.mtn = (d + TM - 1) / TM;
-    a.ntn = (f + TN - 1) / TN;
-    a.C = dw2;
-    a.ldc = f;
-    a.sC = (int64_t)d * f;
-    err = launch_k(a, s);
-    if (err != hipSuccess) return err;
-    F32K b{};
-    b.group_off = g.group_off;
-    b.capacity = g.capacity;
-    b.E = g.E;
-    b.n_rows = g.n_rows;
-    b.A = dgu;
-    b.lda = 2 * f;
-    b.B = x;
-    b.ldb = d;
-    b.M = 2 * f;
-    b.N = d;
-    b.mtn = (2 * f + TM - 1) / TM;
-    b.ntn = (d + TN - 1) / TN;
-    b.C = dw13;
-    b.ldc = d;
-    b.sC = (int64_t)2 * f * d;
-    return launch_k(b, s);
+    switch (op) {
+    case MOE_GEMM_GATE_UP:
+        p.A = (const float*)t.x_perm;
+        p.lda = d;
+        p.B = (const float*)t.w13;
+        p.ldb = d;
+        p.sB = (int64_t)2 * f * d;
+        p.b_mn = false;
+        p.N = f;
+        p.K = d;
+        p.ntn = (f + TN / 2 - 1) / (TN / 2);
+        p.C = (float*)t.gu;
+        p.ldc = 2 * f;
+        p.H = (float*)t.h;
+        p.ldh = f;
+        return launch_m<EPI_SWIGLU_FWD>(p, g.n_rows, s);
+    case MOE_GEMM_DOWN:
+        p.A = (const float*)t.h;
+        p.lda = f;
+        p.B = (const float*)t.w2;
+        p.ldb = f;
+        p.sB = (int64_t)d * f;
+        p.b_mn = false;
+        p.N = d;
+        p.K = f;
+        p.ntn = (d + TN - 1) / TN;
+        p.C = (float*)t.y_perm;
+        p.ldc = d;
+        return launch_m<EPI_STORE>(p, g.n_rows, s);
+    case MOE_GEMM_DGRAD_DOWN:
+        p.A = (const float*)t.dy_perm;
+        p.lda = d;
+        p.B = (const float*)t.w2;
+        p.ldb = f;
+        p.sB = (int64_t)d * f;
+        p.b_mn = true;
+        p.N = f;
+        p.K = d;
+        p.ntn = (f + TN - 1) / TN;
+        p.C = (float*)t.dgu;
+        p.ldc = 2 * f;
+        p.G = (const float*)t.gu;
+        p.ldg = 2 * f;
+        return launch_m<EPI_SWIGLU_BWD>(p, g.n_rows, s);
+    case MOE_GEMM_DGRAD_GATE_UP:
+        p.A = (const float*)t.dgu;
+        p.lda = 2 * f;
+        p.B = (const float*)t.w13;
+        p.ldb = d;
+        p.sB = (int64_t)2 * f * d;
+        p.b_mn = true;
+        p.N = d;
+        p.K = 2 * f;
+        p.ntn = (d + TN - 1) / TN;
+        p.C = (float*)t.dx_perm;
+        p.ldc = d;
+        return launch_m<EPI_STORE>(p, g.n_rows, s);
+    case MOE_GEMM_WGRAD: {
+        F32K k{};
+        k.group_off = g.group_off;
+        k.capacity = g.capacity;
+        k.E = g.E;
+        k.n_rows = g.n_rows;
+        k.nprob = 2;
+        F32KProblem& a = k.pr[0];
+        a.A = (const float*)t.dy_perm;
+        a.lda = d;
+        a.B = (const float*)t.h;
+        a.ldb = f;
+        a.M = d;
+        a.N = f;
+        a.mtn = (d + TM - 1) / TM;
+        a.ntn = (f + TN - 1) / TN;
+        a.C = (float*)t.dw2;
+        a.ldc = f;
+        a.sC = (int64_t)d * f;
+        F32KProblem& b = k.pr[1];
+        b.A = (const float*)t.dgu;
+        b.lda = 2 * f;
+        b.B = (const float*)t.x_perm;
+        b.ldb = d;
+        b.M = 2 * f;
+        b.N = d;
+        b.mtn = (2 * f + TM - 1) / TM;
+        b.ntn = (d + TN - 1) / TN;
+        b.C = (float*)t.dw13;
+        b.ldc = d;
+        b.sC = (int64_t)2 * f * d;
+        return launch_k(k, s);
+    }
+    default:
+        return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace moe

@@ -143,13 +143,21 @@ int moe_grouped_gemm_fwd(int dtype, const void* x_perm, const uint8_t* x_perm_sc
         if (!aligned16(p)) return MOE_EALIGN;
     GroupSpec g{capacity > 0 ? nullptr : group_off, capacity, E, n_rows};
     hipStream_t s = as_stream(stream);
-    if (dtype == MOE_F32)
-        return status_of(gemm_fwd_f32((const float*)x_perm, (const float*)w13, (const float*)w2, g,
-                                      d, f, (float*)gu, (float*)h, (float*)y_perm, s));
-    if (dtype == MOE_BF16)
-        return status_of(gemm_fwd_bf16((const uint16_t*)x_perm, (const uint16_t*)w13,
-                                       (const uint16_t*)w2, g, d, f, (uint16_t*)gu, (uint16_t*)h,
-                                       (uint16_t*)y_perm, s));
+    if (dtype != MOE_MXFP8) {
+        moe_gemm_tensors t{};
+        t.x_perm = x_perm;
+        t.w13 = w13;
+        t.w2 = w2;
+        t.gu = gu;
+        t.h = h;
+        t.y_perm = y_perm;
+        for (int op : {MOE_GEMM_GATE_UP, MOE_GEMM_DOWN}) {
+            const hipError_t e = dtype == MOE_F32 ? gemm_op_f32(op, t, g, d, f, s)
+                                                  : gemm_op_bf16(op, t, g, d, f, s);
+            if (e != hipSuccess) return MOE_EHIP;
+        }
+        return MOE_OK;
+    }
     if (!x_perm_scales || !w13_scales || !w2_scales) return MOE_EINVAL;
     const size_t need = moe_gemm_workspace_bytes(dtype, E, n_rows, d, f);
     if (!ws || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
@@ -174,17 +182,25 @@ int moe_grouped_gemm_bwd(int dtype, const void* dy_perm, const void* x_perm,
         if (!aligned16(p)) return MOE_EALIGN;
     GroupSpec g{capacity > 0 ? nullptr : group_off, capacity, E, n_rows};
     hipStream_t s = as_stream(stream);
-    if (dtype == MOE_F32)
-        return status_of(gemm_bwd_f32((const float*)dy_perm, (const float*)x_perm,
-                                      (const float*)gu, (const float*)h, (const float*)w13,
-                                      (const float*)w2, g, d, f, (float*)dgu, (float*)dx_perm,
-                                      (float*)dw13, (float*)dw2, s));
-    if (dtype == MOE_BF16)
-        return status_of(gemm_bwd_bf16((const uint16_t*)dy_perm, (const uint16_t*)x_perm,
-                                       (const uint16_t*)gu, (const uint16_t*)h,
-                                       (const uint16_t*)w13, (const uint16_t*)w2, g, d, f,
-                                       (uint16_t*)dgu, (uint16_t*)dx_perm, (uint16_t*)dw13,
-                                       (uint16_t*)dw2, s));
+    if (dtype != MOE_MXFP8) {
+        moe_gemm_tensors t{};
+        t.x_perm = x_perm;
+        t.w13 = w13;
+        t.w2 = w2;
+        t.gu = const_cast<void*>(gu);
+        t.h = const_cast<void*>(h);
+        t.dy_perm = dy_perm;
+        t.dgu = dgu;
+        t.dx_perm = dx_perm;
+        t.dw13 = dw13;
+        t.dw2 = dw2;
+        for (int op : {MOE_GEMM_DGRAD_DOWN, MOE_GEMM_DGRAD_GATE_UP, MOE_GEMM_WGRAD}) {
+            const hipError_t e = dtype == MOE_F32 ? gemm_op_f32(op, t, g, d, f, s)
+                                                  : gemm_op_bf16(op, t, g, d, f, s);
+            if (e != hipSuccess) return MOE_EHIP;
+        }
+        return MOE_OK;
+    }
     if (!x_perm_scales || !w13_scales || !w2_scales) return MOE_EINVAL;
     const size_t need = moe_gemm_workspace_bytes(dtype, E, n_rows, d, f);
     if (!ws || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
@@ -193,6 +209,45 @@ int moe_grouped_gemm_bwd(int dtype, const void* dy_perm, const void* x_perm,
                                     (const uint8_t*)w13, w13_scales, (const uint8_t*)w2,
                                     w2_scales, g, d, f, (uint16_t*)dgu, (uint16_t*)dx_perm,
                                     (uint16_t*)dw13, (uint16_t*)dw2, ws, s));
+}
+
+int moe_grouped_gemm_op(int op, int dtype, const moe_gemm_tensors* t,
+                        const int32_t* group_off, int capacity, int E, int64_t n_rows, int d,
+                        int f, moe_stream_t stream)
+{
+    if (!t) return MOE_EINVAL;
+    if (op < MOE_GEMM_GATE_UP || op > MOE_GEMM_WGRAD) return MOE_EINVAL;
+    if (dtype == MOE_MXFP8) return MOE_EUNSUPPORTED;
+    int st = check_gemm_shape(dtype, group_off, capacity, E, n_rows, d, f);
+    if (st != MOE_OK) return st;
+    // operands each stage reads (r) and writes (w)
+    const void* need[4] = {nullptr, nullptr, nullptr, nullptr};
+    int n = 0;
+    switch (op) {
+    case MOE_GEMM_GATE_UP: need[0] = t->x_perm; need[1] = t->w13; need[2] = t->gu; need[3] = t->h; n = 4; break;
+    case MOE_GEMM_DOWN: need[0] = t->h; need[1] = t->w2; need[2] = t->y_perm; n = 3; break;
+    case MOE_GEMM_DGRAD_DOWN: need[0] = t->dy_perm; need[1] = t->w2; need[2] = t->gu; need[3] = t->dgu; n = 4; break;
+    case MOE_GEMM_DGRAD_GATE_UP: need[0] = t->dgu; need[1] = t->w13; need[2] = t->dx_perm; n = 3; break;
+    default: break;
+    }
+    if (op == MOE_GEMM_WGRAD) {
+        const void* wn[6] = {t->dy_perm, t->h, t->dw2, t->dgu, t->x_perm, t->dw13};
+        for (const void* p : wn) {
+            if (!p) return MOE_EINVAL;
+            if (!aligned16(p)) return MOE_EALIGN;
+        }
+    } else {
+        for (int i = 0; i < n; ++i) {
+            const bool weight = need[i] == t->w13 || need[i] == t->w2;
+            if (!need[i] && (weight || n_rows > 0)) return MOE_EINVAL;
+            if (!aligned16(need[i])) return MOE_EALIGN;
+        }
+    }
+    GroupSpec g{capacity > 0 ? nullptr : group_off, capacity, E, n_rows};
+    hipStream_t s = as_stream(stream);
+    const hipError_t e = dtype == MOE_F32 ? gemm_op_f32(op, *t, g, d, f, s)
+                                          : gemm_op_bf16(op, *t, g, d, f, s);
+    return status_of(e);
 }
 
 int moe_quantize_mxfp8(const void* src, int64_t rows, int K, int colwise, const int32_t* group_off,

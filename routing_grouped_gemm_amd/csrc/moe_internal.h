@@ -164,17 +164,10 @@ struct GroupSpec {
     int E;
     int64_t n_rows;
 };
-hipError_t gemm_fwd_bf16(const uint16_t* x, const uint16_t* w13, const uint16_t* w2, GroupSpec g,
-                         int d, int f, uint16_t* gu, uint16_t* h, uint16_t* y, hipStream_t s);
-hipError_t gemm_bwd_bf16(const uint16_t* dy, const uint16_t* x, const uint16_t* gu,
-                         const uint16_t* h, const uint16_t* w13, const uint16_t* w2, GroupSpec g,
-                         int d, int f, uint16_t* dgu, uint16_t* dx, uint16_t* dw13,
-                         uint16_t* dw2, hipStream_t s);
-hipError_t gemm_fwd_f32(const float* x, const float* w13, const float* w2, GroupSpec g, int d,
-                        int f, float* gu, float* h, float* y, hipStream_t s);
-hipError_t gemm_bwd_f32(const float* dy, const float* x, const float* gu, const float* h,
-                        const float* w13, const float* w2, GroupSpec g, int d, int f, float* dgu,
-                        float* dx, float* dw13, float* dw2, hipStream_t s);
+hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, int f,
+                        hipStream_t s);
+hipError_t gemm_op_f32(int op, const moe_gemm_tensors& t, GroupSpec g, int d, int f,
+                       hipStream_t s);
 size_t gemm_ws_mxfp8(int E, int64_t n_rows, int d, int f);
 hipError_t gemm_fwd_mxfp8(const uint8_t* xq, const uint8_t* xs, const uint8_t* w13q,
                           const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
