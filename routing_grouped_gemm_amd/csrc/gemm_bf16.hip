@@ -32,119 +32,211 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-constexpr int BK = 64;
 constexpr int BN = 256;
 constexpr int NTH = 256;
-constexpr int LDT = BK + 8;  // LDS row pitch, bf16 elements (144 bytes)
+constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every range: loads return 0
 
 enum { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2 };
 
-// A ROWS x BK tile source.  K-major: element (r, k) at p[r*ld + k] (rows split
-// into two halves with their own bases and valid counts).  MN-major: element
-// (r, k) at p[k*ld + r].
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over [base, base + bytes); loads at or past `bytes`
+// return zero, which masks tile rows / columns / k outside the operand.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes)
+{
+    const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)(bytes < 0 ? 0 : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off)
+{
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// A ROWS x BK tile source.  K-major: element (r, k) at p[r*ld + k], rows split
+// into two halves with their own bases and valid counts.  MN-major: element
+// (r, k) at p[k*ld + r] with rows0 valid rows.
 struct TileSrc {
     const uint16_t* p0;
     const uint16_t* p1;
     int64_t ld;
-    int rows0, rows1;   // valid rows per half (K-major) / rows0 = valid rows (MN-major)
-    int K;              // valid k
+    int rows0, rows1;
+    int K;
 };
 
-template <int ROWS>
-struct KMajorLoader {
-    static constexpr int NV = ROWS / 32;
-    uint4 v[NV];
-    __device__ __forceinline__ void load(const TileSrc& s, int k0)
-    {
-        const int kc = threadIdx.x & 7;
-        const int rb = threadIdx.x >> 3;
-        const int kk = k0 + kc * 8;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            constexpr int HALF = ROWS / 2;
-            const bool hi = i * 32 >= HALF;
-            const int r = i * 32 + rb - (hi ? HALF : 0);
-            const uint16_t* p = hi ? s.p1 : s.p0;
-            const int nrow = hi ? s.rows1 : s.rows0;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (r < nrow && kk < s.K) val = *reinterpret_cast<const uint4*>(p + r * s.ld + kk);
-            v[i] = val;
-        }
-    }
-    __device__ __forceinline__ void store(uint16_t* lds) const
-    {
-        const int kc = threadIdx.x & 7;
-        const int rb = threadIdx.x >> 3;
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-            *reinterpret_cast<uint4*>(lds + (i * 32 + rb) * LDT + kc * 8) = v[i];
-    }
-};
+// LDS tiles are unpadded and XOR-swizzled in 16-byte chunks (8 bf16):
+//  K-major  [ROWS][BK]: row r at r*BK*2 B.  BK = 64: k-chunk c (of 8) stored at
+//           chunk c ^ ((r >> 1) & 7); BK = 32: chunk c (of 4) at c ^ ((r >> 2) & 3).
+//           The 16 lanes of a 16-byte read (16 consecutive rows, one k-chunk)
+//           then hit 16 distinct bank groups.
+//  MN-major [BK][ROWS]: k-row k at k*ROWS*2 B; row-chunk c stored at chunk
+//           c ^ (4 * (k & 3)).  A transposed read (4 k-rows x 2 chunks per 16
+//           lanes, 2 groups per 32 lanes) then hits 16 distinct bank groups.
+// Both are filled by direct global->LDS loads: every wave instruction writes
+// 1 KB of LDS lane-linearly (16 B per lane), each lane fetching the global
+// element that belongs at its LDS position.
+template <bool MN, int BK>
+__device__ __forceinline__ uint32_t lds_chunk(int row_or_k, int c)
+{
+    if constexpr (MN) return (uint32_t)(c ^ (4 * (row_or_k & 3)));
+    else if constexpr (BK == 64) return (uint32_t)(c ^ ((row_or_k >> 1) & 7));
+    else return (uint32_t)(c ^ ((row_or_k >> 2) & 3));
+}
 
-// MN-major source: each thread owns KB k-rows x 8 rows (KB = 8 for 256 rows,
-// 4 for 128), reads KB 16-byte vectors and transposes them in registers.
-template <int ROWS>
-struct MNMajorLoader {
-    static constexpr int KB = ROWS == 256 ? 8 : 4;
-    static constexpr int NKB = BK / KB;     // k-blocks per tile (8 or 16)
-    uint4 v[KB];
-    __device__ __forceinline__ void load(const TileSrc& s, int k0)
+template <int ROWS, int BK, bool MN>
+struct DirectLoader {
+    static constexpr int TILE_BYTES = ROWS * BK * 2;
+    static constexpr int PER_WAVE = TILE_BYTES / 1024 / 4;   // 1 KB instructions per wave per K-step
+    static constexpr int HALF = ROWS / 2;
+    static constexpr int CPR_K = BK / 8;                     // 16-byte chunks per K-major row
+    static constexpr int RPC_K = 1024 / (BK * 2);            // K-major rows per 1 KB chunk
+    rsrc_t r0, r1;
+    uint32_t off[PER_WAVE];   // per-lane byte offset of its element at k = 0
+    uint32_t kstep;           // bytes a K-step advances (scalar)
+    int K;
+    __device__ __forceinline__ void init(const TileSrc& s)
     {
-        const int rblk = threadIdx.x / NKB;
-        const int kblk = threadIdx.x % NKB;
-        const bool rok = rblk * 8 < s.rows0;
+        const int lane = threadIdx.x & 63;
+        const int w = threadIdx.x >> 6;
+        K = s.K;
+        if constexpr (!MN) {
+            r0 = make_rsrc(s.p0, (int64_t)s.rows0 * s.ld * 2);
+            r1 = make_rsrc(s.p1, (int64_t)s.rows1 * s.ld * 2);
+            kstep = BK * 2;
 #pragma unroll
-        for (int q = 0; q < KB; ++q) {
-            const int k = k0 + kblk * KB + q;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (rok && k < s.K) val = *reinterpret_cast<const uint4*>(s.p0 + (int64_t)k * s.ld + rblk * 8);
-            v[q] = val;
-        }
-    }
-    __device__ __forceinline__ void store(uint16_t* lds) const
-    {
-        const int rblk = threadIdx.x / NKB;
-        const int kblk = threadIdx.x % NKB;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            // k-values of row c: element c of each v[q]
-            uint32_t e[KB];
-#pragma unroll
-            for (int q = 0; q < KB; ++q) {
-                const uint32_t d = (c >> 1) == 0 ? v[q].x : (c >> 1) == 1 ? v[q].y : (c >> 1) == 2 ? v[q].z : v[q].w;
-                e[q] = (c & 1) ? (d >> 16) : (d & 0xffffu);
+            for (int i = 0; i < PER_WAVE; ++i) {
+                const int q = i * 4 + w;
+                const int row = q * RPC_K + lane / CPR_K;
+                const int c = (int)lds_chunk<false, BK>(row, lane % CPR_K);   // XOR is an involution
+                const int rr = row >= HALF ? row - HALF : row;
+                off[i] = (uint32_t)(rr * s.ld * 2 + c * 16);
             }
-            uint16_t* dst = lds + (rblk * 8 + c) * LDT + kblk * KB;
-            if constexpr (KB == 8) {
-                *reinterpret_cast<uint4*>(dst) = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16),
-                                                            e[4] | (e[5] << 16), e[6] | (e[7] << 16));
-            } else {
-                *reinterpret_cast<uint2*>(dst) = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+        } else {
+            r0 = r1 = make_rsrc(s.p0, (int64_t)s.K * s.ld * 2);
+            kstep = (uint32_t)(BK * s.ld * 2);
+            constexpr int KROWS = 1024 / (ROWS * 2);   // k-rows per 1 KB chunk
+            constexpr int CPR = ROWS / 8;              // 16-byte chunks per k-row
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i) {
+                const int q = i * 4 + w;
+                const int k = q * KROWS + lane / CPR;
+                const int c = (int)lds_chunk<true, BK>(k, lane % CPR);
+                off[i] = c * 8 < s.rows0 ? (uint32_t)(k * s.ld * 2 + c * 16) : kOOB;
             }
         }
     }
+    // global -> LDS for K-step kt into the tile at `tile` (TILE_BYTES bytes)
+    __device__ __forceinline__ void issue(uint16_t* tile, int kt)
+    {
+        const int w = threadIdx.x >> 6;
+        const uint32_t so = (uint32_t)kt * kstep;
+        const bool ktail = !MN && (kt + 1) * BK > K;
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int q = i * 4 + w;
+            uint32_t o = off[i];
+            if (ktail) {  // k-chunks at or past K read zero
+                const int lane = threadIdx.x & 63;
+                const int row = q * RPC_K + lane / CPR_K;
+                const int c = (int)lds_chunk<false, BK>(row, lane % CPR_K);
+                if (kt * BK + c * 8 >= K) o = kOOB;
+            }
+            // row block of this instruction: rows [q*RPC_K, ...) lie in the upper half iff q*RPC_K >= HALF
+            const bool hi = !MN && i * 4 * RPC_K >= HALF;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(hi ? r1 : r0,
+                                                     (__attribute__((address_space(3))) void*)(tile + q * 512),
+                                                     16, o, so, 0, 0);
+        }
+    }
 };
 
-template <int ROWS, bool MN>
-using Loader = typename std::conditional<MN, MNMajorLoader<ROWS>, KMajorLoader<ROWS>>::type;
+// One MFMA operand fragment (8 consecutive k of one row) for lane `lane`:
+// tile row row_base + (lane & 31), k = ks*16 + (lane >> 5)*8 + [0, 8).
+template <int ROWS, int BK, bool MN>
+__device__ __forceinline__ bf16x8 read_frag(const uint16_t* tile, int row_base, int ks, int lane)
+{
+    if constexpr (!MN) {
+        const int row = row_base + (lane & 31);
+        const int c = ks * 2 + (lane >> 5);
+        return *reinterpret_cast<const bf16x8*>(tile + row * BK + lds_chunk<false, BK>(row, c) * 8);
+    } else {
+        // 16-lane group g reads rows row_base + (g & 1)*16 + [0,16) at k-chunk (g >> 1):
+        // lanes 4r..4r+3 of the group supply k-row (kb + r), 4 rows each of 16 elements.
+        typedef __attribute__((ext_vector_type(4))) short v4i16;
+        typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+        const int g = lane >> 4;
+        const int j = lane & 15;
+        const int m = row_base + (g & 1) * 16 + 4 * (j & 3);   // first of 4 elements this lane supplies
+        const int kb = ks * 16 + (g >> 1) * 8 + (j >> 2);
+        v4i16 lo, hi;
+        {
+            const int k = kb;
+            const uint16_t* p = tile + k * ROWS + lds_chunk<true, BK>(k, m >> 3) * 8 + (m & 7);
+            lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(__attribute__((address_space(3))) const void*)p);
+        }
+        {
+            const int k = kb + 4;
+            const uint16_t* p = tile + k * ROWS + lds_chunk<true, BK>(k, m >> 3) * 8 + (m & 7);
+            hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(__attribute__((address_space(3))) const void*)p);
+        }
+        typedef __attribute__((ext_vector_type(8))) short v8i16;
+        const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, v);
+    }
+}
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// column (0..255) of the tile that wave column wn, sub-tile j, lane covers
-__device__ __forceinline__ int tile_col(int wn, int j, int lane)
+// first column (0..255) of the 32-wide sub-tile j of wave column wn
+__device__ __forceinline__ int sub_col(int wn, int j) { return (j >> 1) * 128 + wn * 64 + (j & 1) * 32; }
+
+// Accumulator layout.  The MFMA is issued with the B fragment as its first
+// operand, so acc[i][j] holds the transpose of sub-tile (i, j): lane l owns
+// tile row  wm*(BM/2) + 32*i + (l & 31)  and, for g = 0..3, the four
+// consecutive columns  sub_col(wn, j) + 8*g + 4*(l >> 5) + {0,1,2,3}  in
+// acc[i][j][4g .. 4g+3].
+__device__ __forceinline__ int acc_col(int wn, int j, int g, int lane)
 {
-    return (j >> 1) * 128 + wn * 64 + (j & 1) * 32 + (lane & 31);
+    return sub_col(wn, j) + 8 * g + 4 * (lane >> 5);
 }
 
-// BM x 256 tile, K loop over s.K, accumulators acc[BM/64][4]
-template <int BM, bool A_MN, bool B_MN>
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d)
+{
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    const bf16x2 lo = {(__bf16)a, (__bf16)b};
+    const bf16x2 hi = {(__bf16)c, (__bf16)d};
+    return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+__device__ __forceinline__ void unpack4_bf16(uint2 v, float (&o)[4])
+{
+    o[0] = bf16_lo(v.x);
+    o[1] = bf16_hi(v.x);
+    o[2] = bf16_lo(v.y);
+    o[3] = bf16_hi(v.y);
+}
+
+// vmcnt(n) with n known at compile time (expcnt / lgkmcnt left unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// BM x 256 tile over s.K, accumulators acc[BM/64][4].  NS LDS stages of
+// (BM + 256) x BK bf16; the direct loads of the next NS-1 K-steps are in
+// flight while the MFMAs of the current one run; one barrier per K-step.
+template <int BM, int BK, int NS, bool A_MN, bool B_MN>
 __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb, f32x16 (&acc)[BM / 64][4],
                                          uint16_t* smem)
 {
     constexpr int MI = BM / 64;
-    // stage s: A tile at smem + s * STAGE, B tile right after it.  Offsets (not
-    // a table of pointers) keep every access in the LDS address space.
-    constexpr int STAGE = (BM + BN) * LDT;
+    constexpr int STAGE = (BM + BN) * BK;   // elements per stage
+    using LA = DirectLoader<BM, BK, A_MN>;
+    using LB = DirectLoader<BN, BK, B_MN>;
+    constexpr int PER_STEP = LA::PER_WAVE + LB::PER_WAVE;   // load instructions per wave per K-step
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -160,49 +252,67 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb, f
 
     const int nk = (sa.K + BK - 1) / BK;
     if (nk == 0) return;
-    Loader<BM, A_MN> la;
-    Loader<BN, B_MN> lb;
-    la.load(sa, 0);
-    lb.load(sb, 0);
-    la.store(smem);
-    lb.store(smem + BM * LDT);
-    __syncthreads();
-
-    const int arow = wm * (BM / 2) + (lane & 31);
-    const int kofs = (lane >> 5) * 8;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            la.load(sa, (kt + 1) * BK);
-            lb.load(sb, (kt + 1) * BK);
+    LA la;
+    LB lb;
+    la.init(sa);
+    lb.init(sb);
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st) {
+        if (st < nk) {
+            la.issue(smem + st * STAGE, st);
+            lb.issue(smem + st * STAGE + BM * BK, st);
         }
-        const uint16_t* a_s = smem + cur * STAGE;
-        const uint16_t* b_s = a_s + BM * LDT;
+    }
+
+    for (int kt = 0; kt < nk; ++kt) {
+        // loads of K-steps after kt that are already in flight
+        const int ahead = min(NS - 2, nk - 1 - kt);
+        if constexpr (NS >= 4) {
+            if (ahead >= 2) wait_vmcnt<2 * PER_STEP>();
+            else if (ahead == 1) wait_vmcnt<PER_STEP>();
+            else wait_vmcnt<0>();
+        } else if constexpr (NS == 3) {
+            if (ahead >= 1) wait_vmcnt<PER_STEP>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();
+        if (kt + NS - 1 < nk) {
+            uint16_t* nxt = smem + ((kt + NS - 1) % NS) * STAGE;
+            la.issue(nxt, kt + NS - 1);
+            lb.issue(nxt + BM * BK, kt + NS - 1);
+        }
+        const uint16_t* a_s = smem + (kt % NS) * STAGE;
+        const uint16_t* b_s = a_s + BM * BK;
+        // fragments of k-slice ks+1 are read while the MFMAs of slice ks run
+        bf16x8 af[2][MI], bfr[2][4];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) af[0][i] = read_frag<BM, BK, A_MN>(a_s, wm * (BM / 2) + i * 32, 0, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bfr[0][j] = read_frag<BN, BK, B_MN>(b_s, sub_col(wn, j), 0, lane);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8 af[MI], bfr[4];
+            const int c = ks & 1;
+            if (ks + 1 < BK / 16) {
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(a_s + (arow + i * 32) * LDT + ks * 16 + kofs);
+                for (int i = 0; i < MI; ++i)
+                    af[c ^ 1][i] = read_frag<BM, BK, A_MN>(a_s, wm * (BM / 2) + i * 32, ks + 1, lane);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int brow = (j >> 1) * 128 + wn * 64 + (j & 1) * 32 + (lane & 31);
-                bfr[j] = *reinterpret_cast<const bf16x8*>(b_s + brow * LDT + ks * 16 + kofs);
+                for (int j = 0; j < 4; ++j)
+                    bfr[c ^ 1][j] = read_frag<BN, BK, B_MN>(b_s, sub_col(wn, j), ks + 1, lane);
             }
+            // keep the reads of slice ks+1 ahead of the MFMAs of slice ks
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[c][j], af[c][i], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        if (more) {
-            uint16_t* nxt = smem + (cur ^ 1) * STAGE;
-            la.store(nxt);
-            lb.store(nxt + BM * LDT);
-        }
-        __syncthreads();
     }
+    __syncthreads();  // the LDS may be reused by the caller
 }
 
 struct MParams {
@@ -237,52 +347,73 @@ __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][4], cons
     const int wn = wave & 1;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
+        const int row = wm * (BM / 2) + i * 32 + (lane & 31);
+        if (row >= rows_valid) continue;
+        const int64_t grow = row0 + row;
+        if constexpr (EPI == EPI_SWIGLU_FWD) {
+            uint16_t* gu_row = p.C + grow * p.ldc;
+            uint16_t* h_row = p.H + grow * p.ldh;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = wm * (BM / 2) + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            if (row >= rows_valid) continue;
-            const int64_t grow = row0 + row;
-            if constexpr (EPI == EPI_SWIGLU_FWD) {
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int n = nt * 128 + tile_col(wn, j, lane);
+                for (int g = 0; g < 4; ++g) {
+                    const int n = nt * 128 + acc_col(wn, j, g, lane);
                     if (n >= p.f) continue;
-                    const float g = acc[i][j][r];
-                    const float u = acc[i][j + 2][r];
-                    p.C[grow * p.ldc + n] = (uint16_t)f32_to_bf16_bits(g);
-                    p.C[grow * p.ldc + p.f + n] = (uint16_t)f32_to_bf16_bits(u);
-                    p.H[grow * p.ldh + n] = (uint16_t)f32_to_bf16_bits(silu_f(g) * u);
-                }
-            } else {
+                    float gv[4], uv[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int n = nt * BN + tile_col(wn, j, lane);
+                    for (int q = 0; q < 4; ++q) {
+                        gv[q] = acc[i][j][4 * g + q];
+                        uv[q] = acc[i][j + 2][4 * g + q];
+                    }
+                    *reinterpret_cast<uint2*>(gu_row + n) = pack4_bf16(gv[0], gv[1], gv[2], gv[3]);
+                    *reinterpret_cast<uint2*>(gu_row + p.f + n) = pack4_bf16(uv[0], uv[1], uv[2], uv[3]);
+                    *reinterpret_cast<uint2*>(h_row + n) =
+                        pack4_bf16(silu_f(gv[0]) * uv[0], silu_f(gv[1]) * uv[1],
+                                   silu_f(gv[2]) * uv[2], silu_f(gv[3]) * uv[3]);
+                }
+        } else {
+            uint16_t* c_row = p.C + grow * p.ldc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = nt * BN + acc_col(wn, j, g, lane);
                     if (n >= p.N) continue;
-                    const float v = acc[i][j][r];
                     if constexpr (EPI == EPI_STORE) {
-                        p.C[grow * p.ldc + n] = (uint16_t)f32_to_bf16_bits(v);
+                        *reinterpret_cast<uint2*>(c_row + n) =
+                            pack4_bf16(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                       acc[i][j][4 * g + 3]);
                     } else {
-                        const float g = bf16_to_f32(p.G[grow * p.ldg + n]);
-                        const float u = bf16_to_f32(p.G[grow * p.ldg + p.f + n]);
-                        const float s = 1.0f / (1.0f + __expf(-g));
-                        const float da = v * u;
-                        const float du = v * g * s;
-                        const float dg = da * s * (1.0f + g * (1.0f - s));
-                        p.C[grow * p.ldc + n] = (uint16_t)f32_to_bf16_bits(dg);
-                        p.C[grow * p.ldc + p.f + n] = (uint16_t)f32_to_bf16_bits(du);
+                        const uint16_t* g_row = p.G + grow * p.ldg;
+                        float gv[4], uv[4], dg[4], du[4];
+                        unpack4_bf16(*reinterpret_cast<const uint2*>(g_row + n), gv);
+                        unpack4_bf16(*reinterpret_cast<const uint2*>(g_row + p.f + n), uv);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float dh = acc[i][j][4 * g + q];
+                            const float sg = 1.0f / (1.0f + __expf(-gv[q]));
+                            du[q] = dh * gv[q] * sg;
+                            dg[q] = dh * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
+                        }
+                        *reinterpret_cast<uint2*>(c_row + n) = pack4_bf16(dg[0], dg[1], dg[2], dg[3]);
+                        *reinterpret_cast<uint2*>(c_row + p.f + n) = pack4_bf16(du[0], du[1], du[2], du[3]);
                     }
                 }
-            }
         }
     }
 }
 
 // Grouped-M GEMM: C[rows of group e] = A[rows of group e] x B_e^T (B_MN = false:
 // B_e stored [N, K]) or A x B_e (B_MN = true: B_e stored [K, N]).
-template <int BM, bool B_MN, int EPI>
-__global__ __launch_bounds__(NTH, 1) void gemm_grouped_m_kernel(MParams p)
+// one 256-thread workgroup per CU: each SIMD runs one wave that may use the
+// whole register file (accumulators in AGPRs)
+#define MOE_GEMM_KERNEL_ATTRS \
+    __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1), amdgpu_flat_work_group_size(NTH, NTH)))
+
+template <int BM, int BK, int NS, bool B_MN, int EPI>
+__global__ MOE_GEMM_KERNEL_ATTRS void gemm_grouped_m_kernel(MParams p)
 {
-    __shared__ __align__(16) uint16_t smem[2 * (BM + BN) * LDT];
+    __shared__ __align__(16) uint16_t smem[NS * (BM + BN) * BK];
     __shared__ int s_pref[kMaxExperts + 1];
     __shared__ int s_part[NTH];
 
@@ -336,7 +467,7 @@ __global__ __launch_bounds__(NTH, 1) void gemm_grouped_m_kernel(MParams p)
     }
 
     f32x16 acc[BM / 64][4];
-    mainloop<BM, false, B_MN>(sa, sb, acc, smem);
+    mainloop<BM, BK, NS, false, B_MN>(sa, sb, acc, smem);
     epilogue_m<BM, EPI>(acc, p, row0, rows_valid, nt);
 }
 
@@ -362,10 +493,10 @@ struct KParams {
 // Grouped-K GEMM (weight gradients): C_e = A_e^T B_e over the rows of group e,
 // for one or two problems sharing the groups.  Tiles are expert-major so the
 // tiles reading one expert's rows run together on one XCD.
-template <int BM>
-__global__ __launch_bounds__(NTH, 1) void gemm_grouped_k_kernel(KParams p)
+template <int BM, int BK, int NS>
+__global__ MOE_GEMM_KERNEL_ATTRS void gemm_grouped_k_kernel(KParams p)
 {
-    __shared__ __align__(16) uint16_t smem[2 * (BM + BN) * LDT];
+    __shared__ __align__(16) uint16_t smem[NS * (BM + BN) * BK];
     const int t0 = p.pr[0].mtn * p.pr[0].ntn;
     const int tiles_e = t0 + (p.nprob > 1 ? p.pr[1].mtn * p.pr[1].ntn : 0);
     const int total = p.E * tiles_e;
@@ -399,7 +530,7 @@ __global__ __launch_bounds__(NTH, 1) void gemm_grouped_k_kernel(KParams p)
     sb.K = m_e;
 
     f32x16 acc[BM / 64][4];
-    mainloop<BM, true, true>(sa, sb, acc, smem);
+    mainloop<BM, BK, NS, true, true>(sa, sb, acc, smem);
 
     constexpr int MI = BM / 64;
     const int tid = threadIdx.x;
@@ -409,32 +540,36 @@ __global__ __launch_bounds__(NTH, 1) void gemm_grouped_k_kernel(KParams p)
     const int wn = wave & 1;
     uint16_t* Ce = q.C + (int64_t)e * q.sC;
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+        const int m = mt * BM + wm * (BM / 2) + i * 32 + (lane & 31);
+        if (m >= q.M) continue;
+        uint16_t* c_row = Ce + (int64_t)m * q.ldc;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = mt * BM + wm * (BM / 2) + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            if (m >= q.M) continue;
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = nt * BN + tile_col(wn, j, lane);
-                if (n < q.N) Ce[(int64_t)m * q.ldc + n] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+            for (int g = 0; g < 4; ++g) {
+                const int n = nt * BN + acc_col(wn, j, g, lane);
+                if (n < q.N)
+                    *reinterpret_cast<uint2*>(c_row + n) =
+                        pack4_bf16(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                   acc[i][j][4 * g + 3]);
             }
-        }
+    }
 }
 
-template <int BM, bool B_MN, int EPI>
+template <int BM, int BK, int NS, bool B_MN, int EPI>
 hipError_t launch_m(const MParams& p, int64_t n_rows, hipStream_t s)
 {
     // host-known bound on the M-tiles: sum ceil(m_e / BM) <= n_rows / BM + E
     const int64_t bound = (n_rows / BM + p.E) * (int64_t)p.ntn;
     const int64_t grid = (bound + 7) / 8 * 8;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_grouped_m_kernel<BM, B_MN, EPI>), dim3((unsigned)grid), dim3(NTH), 0,
+    hipLaunchKernelGGL((gemm_grouped_m_kernel<BM, BK, NS, B_MN, EPI>), dim3((unsigned)grid), dim3(NTH), 0,
                        s, p);
     return hipGetLastError();
 }
 
-template <int BM>
+template <int BM, int BK, int NS>
 hipError_t launch_k(const KParams& p, hipStream_t s)
 {
     int64_t tiles_e = 0;
@@ -442,11 +577,26 @@ hipError_t launch_k(const KParams& p, hipStream_t s)
     const int64_t total = (int64_t)p.E * tiles_e;
     const int64_t grid = (total + 7) / 8 * 8;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_grouped_k_kernel<BM>), dim3((unsigned)grid), dim3(NTH), 0, s, p);
+    hipLaunchKernelGGL((gemm_grouped_k_kernel<BM, BK, NS>), dim3((unsigned)grid), dim3(NTH), 0, s, p);
     return hipGetLastError();
 }
 
-constexpr int kBM = 128;
+#ifndef MOE_GEMM_BM_M
+#define MOE_GEMM_BM_M 256
+#endif
+#ifndef MOE_GEMM_BM_K
+#define MOE_GEMM_BM_K 256
+#endif
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 64
+#endif
+#ifndef MOE_GEMM_NS
+#define MOE_GEMM_NS 2
+#endif
+constexpr int kBM = MOE_GEMM_BM_M;   // M tile of the grouped-M (forward / dgrad) GEMMs
+constexpr int kBMK = MOE_GEMM_BM_K;  // M tile of the grouped-K (weight gradient) GEMM
+constexpr int kBK = MOE_GEMM_BK;     // K step
+constexpr int kNS = MOE_GEMM_NS;     // LDS pipeline stages
 
 }  // namespace
 
@@ -473,7 +623,7 @@ hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, i
         p.ldc = 2 * f;
         p.H = (uint16_t*)t.h;
         p.ldh = f;
-        return launch_m<kBM, false, EPI_SWIGLU_FWD>(p, g.n_rows, s);
+        return launch_m<kBM, kBK, kNS, false, EPI_SWIGLU_FWD>(p, g.n_rows, s);
     case MOE_GEMM_DOWN:  // y = h Wd^T
         p.A = (const uint16_t*)t.h;
         p.lda = f;
@@ -485,7 +635,7 @@ hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, i
         p.ntn = (d + BN - 1) / BN;
         p.C = (uint16_t*)t.y_perm;
         p.ldc = d;
-        return launch_m<kBM, false, EPI_STORE>(p, g.n_rows, s);
+        return launch_m<kBM, kBK, kNS, false, EPI_STORE>(p, g.n_rows, s);
     case MOE_GEMM_DGRAD_DOWN:  // dh = dy Wd (Wd_e stored [d, f] = [K, N]), SwiGLU backward
         p.A = (const uint16_t*)t.dy_perm;
         p.lda = d;
@@ -499,7 +649,7 @@ hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, i
         p.ldc = 2 * f;
         p.G = (const uint16_t*)t.gu;
         p.ldg = 2 * f;
-        return launch_m<kBM, true, EPI_SWIGLU_BWD>(p, g.n_rows, s);
+        return launch_m<kBM, kBK, kNS, true, EPI_SWIGLU_BWD>(p, g.n_rows, s);
     case MOE_GEMM_DGRAD_GATE_UP:  // dx = [dg | du] [Wg ; Wu] (W13_e stored [2f, d] = [K, N])
         p.A = (const uint16_t*)t.dgu;
         p.lda = 2 * f;
@@ -511,7 +661,7 @@ hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, i
         p.ntn = (d + BN - 1) / BN;
         p.C = (uint16_t*)t.dx_perm;
         p.ldc = d;
-        return launch_m<kBM, true, EPI_STORE>(p, g.n_rows, s);
+        return launch_m<kBM, kBK, kNS, true, EPI_STORE>(p, g.n_rows, s);
     case MOE_GEMM_WGRAD: {  // dWd_e [d, f] = dy_e^T h_e ; dW13_e [2f, d] = dgu_e^T x_e
         KParams k{};
         k.group_off = g.group_off;
@@ -526,7 +676,7 @@ hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, i
         a.ldb = f;
         a.M = d;
         a.N = f;
-        a.mtn = (d + kBM - 1) / kBM;
+        a.mtn = (d + kBMK - 1) / kBMK;
         a.ntn = (f + BN - 1) / BN;
         a.C = (uint16_t*)t.dw2;
         a.ldc = f;
@@ -538,12 +688,12 @@ hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, i
         b.ldb = d;
         b.M = 2 * f;
         b.N = d;
-        b.mtn = (2 * f + kBM - 1) / kBM;
+        b.mtn = (2 * f + kBMK - 1) / kBMK;
         b.ntn = (d + BN - 1) / BN;
         b.C = (uint16_t*)t.dw13;
         b.ldc = d;
         b.sC = (int64_t)2 * f * d;
-        return launch_k<kBM>(k, s);
+        return launch_k<kBMK, kBK, kNS>(k, s);
     }
     default:
         return hipErrorInvalidValue;
