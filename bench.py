@@ -42,6 +42,45 @@ KERNEL_NAMES = {
 }
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {"gemm": "routing_grouped_gemm_amd/csrc/gemm_bf16.hip",
+                  "route": "routing_grouped_gemm_amd/csrc/route.hip",
+                  "permute": "routing_grouped_gemm_amd/csrc/permute.hip",
+                  "combine": "routing_grouped_gemm_amd/csrc/permute.hip"}
+
+
+def source_hash(stage):
+    import hashlib
+    key = "gemm" if stage.startswith("gemm") else stage.split("_")[0]
+    path = os.path.join(ROOT, KERNEL_SOURCES.get(key, KERNEL_SOURCES["gemm"]))
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(stage, workload):
+    """HBM bytes per launch of `stage` from the committed counter record
+    (profiles/traffic_<stage>_<workload>.json), or None when there is none or
+    the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"traffic_{stage}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256_16") != source_hash(stage):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(nbytes=1 << 31, iters=5):
+    """A plain device copy of known size (for scaling FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    b = torch.empty_like(a)
+    for _ in range(iters):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes,
+                      "iters": iters}), flush=True)
+
+
 def roofline(attainable_peak, bandwidth, intensity):
     """Attainable throughput = min(peak compute, peak bandwidth x intensity)."""
     return min(attainable_peak, bandwidth * intensity)
@@ -200,7 +239,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=1,
                     help="experts whose rows the CPU-oracle sample covers")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 2 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not "
               "supported (this build runs on exactly one GPU).", file=sys.stderr)
@@ -238,7 +282,9 @@ def main():
     else:
         rl = {"bound": "hbm", "achieved": round(by / dom_ms / 1e6, 1), "peak": PEAK_HBM_GBS,
               "unit": "GB/s", "frac": round(by / dom_ms / 1e6 / PEAK_HBM_GBS, 4)}
-    rl.update({"traffic": None, "kernel": KERNEL_NAMES.get(dom, dom), "stage": dom,
+    rl["attainable"] = round(roofline(peak, PEAK_HBM_GBS / 1e3, fl / by), 1) if fl else None
+    rl.update({"traffic": measured_traffic(dom, args.workload + ("_padded" if args.padded else "")),
+               "kernel": KERNEL_NAMES.get(dom, dom), "stage": dom,
                "launch_ms": round(dom_ms, 4), "algorithmic_flops": fl, "algorithmic_bytes": by})
     value = T / (res["ms_per_step"] / 1e3)
     out = {

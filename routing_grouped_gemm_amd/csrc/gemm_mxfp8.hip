@@ -1,9 +1,10 @@
 // MXFP8 grouped GEMMs: not provided yet.  The entry points report
-// MOE_EUNSUPPORTED through a launch error so callers never receive silently
-// wrong results.
+// MOE_EUNSUPPORTED so callers never receive silently wrong results.
 #include "moe_internal.h"
 
 namespace moe {
+
+const bool kMxGemmAvailable = false;
 
 size_t gemm_ws_mxfp8(int E, int64_t n_rows, int d, int f)
 {

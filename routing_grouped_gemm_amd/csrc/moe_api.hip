@@ -161,6 +161,7 @@ int moe_grouped_gemm_fwd(int dtype, const void* x_perm, const uint8_t* x_perm_sc
     if (!x_perm_scales || !w13_scales || !w2_scales) return MOE_EINVAL;
     const size_t need = moe_gemm_workspace_bytes(dtype, E, n_rows, d, f);
     if (!ws || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
+    if (!kMxGemmAvailable) return MOE_EUNSUPPORTED;
     return status_of(gemm_fwd_mxfp8((const uint8_t*)x_perm, x_perm_scales, (const uint8_t*)w13,
                                     w13_scales, (const uint8_t*)w2, w2_scales, g, d, f,
                                     (uint16_t*)gu, (uint16_t*)h, (uint16_t*)y_perm, ws, s));
@@ -204,6 +205,7 @@ int moe_grouped_gemm_bwd(int dtype, const void* dy_perm, const void* x_perm,
     if (!x_perm_scales || !w13_scales || !w2_scales) return MOE_EINVAL;
     const size_t need = moe_gemm_workspace_bytes(dtype, E, n_rows, d, f);
     if (!ws || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
+    if (!kMxGemmAvailable) return MOE_EUNSUPPORTED;
     return status_of(gemm_bwd_mxfp8((const uint16_t*)dy_perm, (const uint8_t*)x_perm,
                                     x_perm_scales, (const uint16_t*)gu, (const uint16_t*)h,
                                     (const uint8_t*)w13, w13_scales, (const uint8_t*)w2,
