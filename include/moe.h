@@ -36,8 +36,8 @@
  *   - Calls are stateless and re-entrant; results are bitwise reproducible
  *     for identical inputs (no floating-point atomics anywhere).
  *   - Limits: 1 <= E <= 1024, 1 <= k <= min(E, 8), row widths d and f
- *     multiples of 8 (of 32 for MXFP8), all pointers 16-byte aligned, n_rows
- *     * max(d, 2f) < 2^31.
+ *     multiples of 8 (MXFP8: 32 for the permute / quantiser, 128 for the
+ *     grouped GEMMs), all pointers 16-byte aligned, n_rows < 2^31.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -255,13 +255,15 @@ MOE_API int moe_unpermute_combine(int dtype, const void* y_perm, const int32_t* 
  * colwise = 1     blocks of 32 along the rows inside each group
  *                 [group_off[g], group_off[g+1]) (device int32, n_groups+1
  *                 entries; NULL = one group of all rows).  Output is each
- *                 group transposed, rows padded to a multiple of 32 with zero
- *                 codes: group g occupies codes[K * P_g .. K * P_{g+1}) as
- *                 [K][P_{g+1} - P_g] and scales[K * P_g / 32 ..) as
- *                 [K][(P_{g+1} - P_g) / 32], where P_g = sum over earlier groups
- *                 of their row count rounded up to 32.  The buffers must hold
- *                 K * (rows + 32 * n_groups) codes and 1/32 of that in scales.
+ *                 group transposed, its rows padded with zero codes to a
+ *                 multiple of MOE_MX_COL_PAD (128): group g occupies
+ *                 codes[K * P_g .. K * P_{g+1}) as [K][P_{g+1} - P_g] and
+ *                 scales[K * P_g / 32 ..) as [K][(P_{g+1} - P_g) / 32], where
+ *                 P_g = sum over earlier groups of their row count rounded up
+ *                 to 128.  The buffers must hold K * (rows + 128 * n_groups)
+ *                 codes and 1/32 of that in scales.
  */
+#define MOE_MX_COL_PAD 128
 MOE_API int moe_quantize_mxfp8(const void* src, int64_t rows, int K, int colwise,
                        const int32_t* group_off, int n_groups, uint8_t* codes,
                        uint8_t* scales, moe_stream_t stream);

@@ -154,8 +154,9 @@ def moe_grouped_gemm_fwd(dtype, x_perm, w13, w2, group_off, capacity, gu, h, y_p
                          x_perm_scales=None, w13_scales=None, w2_scales=None, ws=None,
                          stream=None):
     """x_perm [n_rows, d], w13 [E, 2f, d], w2 [E, d, f] -> gu [n_rows, 2f], h [n_rows, f],
-    y_perm [n_rows, d].  group_off [E+1] device int32 (ignored when capacity > 0)."""
-    E = w13.shape[0]
+    y_perm [n_rows, d].  group_off [E+1] device int32 (ignored when capacity > 0, but its
+    length still gives E)."""
+    E = group_off.numel() - 1
     n_rows, d = x_perm.shape
     f = h.shape[1]
     rc = load().moe_grouped_gemm_fwd(dtype, _p(x_perm), _p(x_perm_scales), _p(w13),
@@ -169,7 +170,7 @@ def moe_grouped_gemm_bwd(dtype, dy_perm, x_perm, gu, h, w13, w2, group_off, capa
                          dx_perm, dw13, dw2, x_perm_scales=None, w13_scales=None, w2_scales=None,
                          ws=None, stream=None):
     """Activation and weight gradients of the grouped SwiGLU FFN (see include/moe.h)."""
-    E = dw13.shape[0]
+    E = group_off.numel() - 1
     n_rows, d = dy_perm.shape
     f = h.shape[1]
     rc = load().moe_grouped_gemm_bwd(dtype, _p(dy_perm), _p(x_perm), _p(x_perm_scales), _p(gu),

@@ -24,132 +24,12 @@
 //     formed in registers and g, u, h are stored); the SwiGLU backward (reads
 //     the saved g, u of its elements and stores dg, du).
 // Accumulation is fp32; bf16 results are rounded to nearest even.
-#include "moe_internal.h"
+#include "gemm_common.h"
 
 namespace moe {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-
-constexpr int BN = 256;
-constexpr int NTH = 256;
-constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every range: loads return 0
-
-enum { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2 };
-
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Raw buffer resource over [base, base + bytes); loads at or past `bytes`
-// return zero, which masks tile rows / columns / k outside the operand.
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes)
-{
-    const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)(bytes < 0 ? 0 : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off)
-{
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-// A ROWS x BK tile source.  K-major: element (r, k) at p[r*ld + k], rows split
-// into two halves with their own bases and valid counts.  MN-major: element
-// (r, k) at p[k*ld + r] with rows0 valid rows.
-struct TileSrc {
-    const uint16_t* p0;
-    const uint16_t* p1;
-    int64_t ld;
-    int rows0, rows1;
-    int K;
-};
-
-// LDS tiles are unpadded and XOR-swizzled in 16-byte chunks (8 bf16):
-//  K-major  [ROWS][BK]: row r at r*BK*2 B.  BK = 64: k-chunk c (of 8) stored at
-//           chunk c ^ ((r >> 1) & 7); BK = 32: chunk c (of 4) at c ^ ((r >> 2) & 3).
-//           The 16 lanes of a 16-byte read (16 consecutive rows, one k-chunk)
-//           then hit 16 distinct bank groups.
-//  MN-major [BK][ROWS]: k-row k at k*ROWS*2 B; row-chunk c stored at chunk
-//           c ^ (4 * (k & 3)).  A transposed read (4 k-rows x 2 chunks per 16
-//           lanes, 2 groups per 32 lanes) then hits 16 distinct bank groups.
-// Both are filled by direct global->LDS loads: every wave instruction writes
-// 1 KB of LDS lane-linearly (16 B per lane), each lane fetching the global
-// element that belongs at its LDS position.
-template <bool MN, int BK>
-__device__ __forceinline__ uint32_t lds_chunk(int row_or_k, int c)
-{
-    if constexpr (MN) return (uint32_t)(c ^ (4 * (row_or_k & 3)));
-    else if constexpr (BK == 64) return (uint32_t)(c ^ ((row_or_k >> 1) & 7));
-    else return (uint32_t)(c ^ ((row_or_k >> 2) & 3));
-}
-
-template <int ROWS, int BK, bool MN>
-struct DirectLoader {
-    static constexpr int TILE_BYTES = ROWS * BK * 2;
-    static constexpr int PER_WAVE = TILE_BYTES / 1024 / 4;   // 1 KB instructions per wave per K-step
-    static constexpr int HALF = ROWS / 2;
-    static constexpr int CPR_K = BK / 8;                     // 16-byte chunks per K-major row
-    static constexpr int RPC_K = 1024 / (BK * 2);            // K-major rows per 1 KB chunk
-    rsrc_t r0, r1;
-    uint32_t off[PER_WAVE];   // per-lane byte offset of its element at k = 0
-    uint32_t kstep;           // bytes a K-step advances (scalar)
-    int K;
-    __device__ __forceinline__ void init(const TileSrc& s)
-    {
-        const int lane = threadIdx.x & 63;
-        const int w = threadIdx.x >> 6;
-        K = s.K;
-        if constexpr (!MN) {
-            r0 = make_rsrc(s.p0, (int64_t)s.rows0 * s.ld * 2);
-            r1 = make_rsrc(s.p1, (int64_t)s.rows1 * s.ld * 2);
-            kstep = BK * 2;
-#pragma unroll
-            for (int i = 0; i < PER_WAVE; ++i) {
-                const int q = i * 4 + w;
-                const int row = q * RPC_K + lane / CPR_K;
-                const int c = (int)lds_chunk<false, BK>(row, lane % CPR_K);   // XOR is an involution
-                const int rr = row >= HALF ? row - HALF : row;
-                off[i] = (uint32_t)(rr * s.ld * 2 + c * 16);
-            }
-        } else {
-            r0 = r1 = make_rsrc(s.p0, (int64_t)s.K * s.ld * 2);
-            kstep = (uint32_t)(BK * s.ld * 2);
-            constexpr int KROWS = 1024 / (ROWS * 2);   // k-rows per 1 KB chunk
-            constexpr int CPR = ROWS / 8;              // 16-byte chunks per k-row
-#pragma unroll
-            for (int i = 0; i < PER_WAVE; ++i) {
-                const int q = i * 4 + w;
-                const int k = q * KROWS + lane / CPR;
-                const int c = (int)lds_chunk<true, BK>(k, lane % CPR);
-                off[i] = c * 8 < s.rows0 ? (uint32_t)(k * s.ld * 2 + c * 16) : kOOB;
-            }
-        }
-    }
-    // global -> LDS for K-step kt into the tile at `tile` (TILE_BYTES bytes)
-    __device__ __forceinline__ void issue(uint16_t* tile, int kt)
-    {
-        const int w = threadIdx.x >> 6;
-        const uint32_t so = (uint32_t)kt * kstep;
-        const bool ktail = !MN && (kt + 1) * BK > K;
-#pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) {
-            const int q = i * 4 + w;
-            uint32_t o = off[i];
-            if (ktail) {  // k-chunks at or past K read zero
-                const int lane = threadIdx.x & 63;
-                const int row = q * RPC_K + lane / CPR_K;
-                const int c = (int)lds_chunk<false, BK>(row, lane % CPR_K);
-                if (kt * BK + c * 8 >= K) o = kOOB;
-            }
-            // row block of this instruction: rows [q*RPC_K, ...) lie in the upper half iff q*RPC_K >= HALF
-            const bool hi = !MN && i * 4 * RPC_K >= HALF;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(hi ? r1 : r0,
-                                                     (__attribute__((address_space(3))) void*)(tile + q * 512),
-                                                     16, o, so, 0, 0);
-        }
-    }
-};
+using namespace gemm;
 
 // One MFMA operand fragment (8 consecutive k of one row) for lane `lane`:
 // tile row row_base + (lane & 31), k = ks*16 + (lane >> 5)*8 + [0, 8).
@@ -184,45 +64,6 @@ __device__ __forceinline__ bf16x8 read_frag(const uint16_t* tile, int row_base, 
         const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         return __builtin_bit_cast(bf16x8, v);
     }
-}
-
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
-
-// first column (0..255) of the 32-wide sub-tile j of wave column wn
-__device__ __forceinline__ int sub_col(int wn, int j) { return (j >> 1) * 128 + wn * 64 + (j & 1) * 32; }
-
-// Accumulator layout.  The MFMA is issued with the B fragment as its first
-// operand, so acc[i][j] holds the transpose of sub-tile (i, j): lane l owns
-// tile row  wm*(BM/2) + 32*i + (l & 31)  and, for g = 0..3, the four
-// consecutive columns  sub_col(wn, j) + 8*g + 4*(l >> 5) + {0,1,2,3}  in
-// acc[i][j][4g .. 4g+3].
-__device__ __forceinline__ int acc_col(int wn, int j, int g, int lane)
-{
-    return sub_col(wn, j) + 8 * g + 4 * (lane >> 5);
-}
-
-__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d)
-{
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-    const bf16x2 lo = {(__bf16)a, (__bf16)b};
-    const bf16x2 hi = {(__bf16)c, (__bf16)d};
-    return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-}
-
-__device__ __forceinline__ void unpack4_bf16(uint2 v, float (&o)[4])
-{
-    o[0] = bf16_lo(v.x);
-    o[1] = bf16_hi(v.x);
-    o[2] = bf16_lo(v.y);
-    o[3] = bf16_hi(v.y);
-}
-
-// vmcnt(n) with n known at compile time (expcnt / lgkmcnt left unconstrained)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // BM x 256 tile over s.K, accumulators acc[BM/64][4].  NS LDS stages of
@@ -315,101 +156,8 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb, f
     __syncthreads();  // the LDS may be reused by the caller
 }
 
-struct MParams {
-    const uint16_t* A;     // grouped rows, K-major [n_rows, K]
-    int64_t lda;
-    const uint16_t* B;     // per-expert weight: B + e * sB
-    int64_t ldb, sB;
-    int N;                 // output columns (f for the SwiGLU forward)
-    int K;
-    const int32_t* group_off;
-    int capacity, E;
-    int64_t n_rows;
-    int ntn;               // N tiles
-    uint16_t* C;           // STORE: out; SWIGLU_FWD: gu; SWIGLU_BWD: dgu
-    int64_t ldc;
-    uint16_t* H;           // SWIGLU_FWD: h
-    int64_t ldh;
-    const uint16_t* G;     // SWIGLU_BWD: saved gu
-    int64_t ldg;
-    int f;                 // SWIGLU: column offset of the u half in gu / dgu
-};
-
-template <int BM, int EPI>
-__device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][4], const MParams& p,
-                                           int64_t row0, int rows_valid, int nt)
-{
-    constexpr int MI = BM / 64;
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-        const int row = wm * (BM / 2) + i * 32 + (lane & 31);
-        if (row >= rows_valid) continue;
-        const int64_t grow = row0 + row;
-        if constexpr (EPI == EPI_SWIGLU_FWD) {
-            uint16_t* gu_row = p.C + grow * p.ldc;
-            uint16_t* h_row = p.H + grow * p.ldh;
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = nt * 128 + acc_col(wn, j, g, lane);
-                    if (n >= p.f) continue;
-                    float gv[4], uv[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        gv[q] = acc[i][j][4 * g + q];
-                        uv[q] = acc[i][j + 2][4 * g + q];
-                    }
-                    *reinterpret_cast<uint2*>(gu_row + n) = pack4_bf16(gv[0], gv[1], gv[2], gv[3]);
-                    *reinterpret_cast<uint2*>(gu_row + p.f + n) = pack4_bf16(uv[0], uv[1], uv[2], uv[3]);
-                    *reinterpret_cast<uint2*>(h_row + n) =
-                        pack4_bf16(silu_f(gv[0]) * uv[0], silu_f(gv[1]) * uv[1],
-                                   silu_f(gv[2]) * uv[2], silu_f(gv[3]) * uv[3]);
-                }
-        } else {
-            uint16_t* c_row = p.C + grow * p.ldc;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = nt * BN + acc_col(wn, j, g, lane);
-                    if (n >= p.N) continue;
-                    if constexpr (EPI == EPI_STORE) {
-                        *reinterpret_cast<uint2*>(c_row + n) =
-                            pack4_bf16(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                       acc[i][j][4 * g + 3]);
-                    } else {
-                        const uint16_t* g_row = p.G + grow * p.ldg;
-                        float gv[4], uv[4], dg[4], du[4];
-                        unpack4_bf16(*reinterpret_cast<const uint2*>(g_row + n), gv);
-                        unpack4_bf16(*reinterpret_cast<const uint2*>(g_row + p.f + n), uv);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float dh = acc[i][j][4 * g + q];
-                            const float sg = 1.0f / (1.0f + __expf(-gv[q]));
-                            du[q] = dh * gv[q] * sg;
-                            dg[q] = dh * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
-                        }
-                        *reinterpret_cast<uint2*>(c_row + n) = pack4_bf16(dg[0], dg[1], dg[2], dg[3]);
-                        *reinterpret_cast<uint2*>(c_row + p.f + n) = pack4_bf16(du[0], du[1], du[2], du[3]);
-                    }
-                }
-        }
-    }
-}
-
 // Grouped-M GEMM: C[rows of group e] = A[rows of group e] x B_e^T (B_MN = false:
 // B_e stored [N, K]) or A x B_e (B_MN = true: B_e stored [K, N]).
-// one 256-thread workgroup per CU: each SIMD runs one wave that may use the
-// whole register file (accumulators in AGPRs)
-#define MOE_GEMM_KERNEL_ATTRS \
-    __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1), amdgpu_flat_work_group_size(NTH, NTH)))
-
 template <int BM, int BK, int NS, bool B_MN, int EPI>
 __global__ MOE_GEMM_KERNEL_ATTRS void gemm_grouped_m_kernel(MParams p)
 {
@@ -418,23 +166,11 @@ __global__ MOE_GEMM_KERNEL_ATTRS void gemm_grouped_m_kernel(MParams p)
     __shared__ int s_part[NTH];
 
     // device tile schedule: expert-major, N-tile, then M-tile
-    const int total =
-        block_tile_prefix<NTH>(p.group_off, p.capacity, p.E, p.n_rows, BM, p.ntn, s_pref, s_part);
-    const int per_xcd = (total + 7) / 8;
-    const int xcd = blockIdx.x % 8;
-    const int slot = blockIdx.x / 8;
-    if (slot >= per_xcd) return;
-    const int L = xcd * per_xcd + slot;
-    if (L >= total) return;
-    const int e = find_group(s_pref, p.E, L);
-    const int64_t g0 = group_begin(p.group_off, p.capacity, e, p.n_rows);
-    const int m_e = (int)group_rows(p.group_off, p.capacity, e, p.n_rows);
-    const int mt_e = (m_e + BM - 1) / BM;
-    const int local = L - s_pref[e];
-    const int nt = local / mt_e;
-    const int mt = local - nt * mt_e;
-    const int64_t row0 = g0 + (int64_t)mt * BM;
-    const int rows_valid = min(BM, m_e - mt * BM);
+    MTile tile;
+    if (!schedule_m<BM, NTH>(p.group_off, p.capacity, p.E, p.n_rows, p.ntn, s_pref, s_part, tile)) return;
+    const int e = tile.e, nt = tile.nt;
+    const int64_t row0 = tile.row0;
+    const int rows_valid = tile.rows_valid;
 
     TileSrc sa;
     sa.p0 = p.A + row0 * p.lda;
@@ -470,6 +206,8 @@ __global__ MOE_GEMM_KERNEL_ATTRS void gemm_grouped_m_kernel(MParams p)
     mainloop<BM, BK, NS, false, B_MN>(sa, sb, acc, smem);
     epilogue_m<BM, EPI>(acc, p, row0, rows_valid, nt);
 }
+
+
 
 struct KProblem {
     const uint16_t* A;     // [n_rows, M] (M contiguous); group e's rows are its K
@@ -532,29 +270,8 @@ __global__ MOE_GEMM_KERNEL_ATTRS void gemm_grouped_k_kernel(KParams p)
     f32x16 acc[BM / 64][4];
     mainloop<BM, BK, NS, true, true>(sa, sb, acc, smem);
 
-    constexpr int MI = BM / 64;
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
-    uint16_t* Ce = q.C + (int64_t)e * q.sC;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-        const int m = mt * BM + wm * (BM / 2) + i * 32 + (lane & 31);
-        if (m >= q.M) continue;
-        uint16_t* c_row = Ce + (int64_t)m * q.ldc;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = nt * BN + acc_col(wn, j, g, lane);
-                if (n < q.N)
-                    *reinterpret_cast<uint2*>(c_row + n) =
-                        pack4_bf16(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                   acc[i][j][4 * g + 3]);
-            }
-    }
+    store_tile<BM>(acc, q.C + (int64_t)e * q.sC + (int64_t)mt * BM * q.ldc, q.ldc, 0, q.M - mt * BM,
+                   nt * BN, q.N);
 }
 
 template <int BM, int BK, int NS, bool B_MN, int EPI>

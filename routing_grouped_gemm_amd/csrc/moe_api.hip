@@ -27,7 +27,8 @@ int check_gemm_shape(int dtype, const int32_t* group_off, int capacity, int E, i
         return MOE_EINVAL;
     if (capacity > 0 && (int64_t)E * capacity != n_rows) return MOE_EINVAL;
     if (capacity == 0 && !group_off) return MOE_EINVAL;
-    const int unit = dtype == MOE_MXFP8 ? 32 : (dtype == MOE_F32 ? 4 : 8);
+    // MXFP8 GEMMs step K by 128 fp8 (whole 4-byte scale words per row)
+    const int unit = dtype == MOE_MXFP8 ? 128 : (dtype == MOE_F32 ? 4 : 8);
     if (d % unit || f % unit) return MOE_EALIGN;
     if (n_rows * (int64_t)(d > 2 * f ? d : 2 * f) >= ((int64_t)1 << 40)) return MOE_EINVAL;
     return MOE_OK;

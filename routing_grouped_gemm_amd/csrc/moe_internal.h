@@ -132,6 +132,7 @@ __device__ __forceinline__ int find_group(const int* s_pref, int E, int L)
 constexpr int kRouteTokensPerBlock = 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 8;
+constexpr int kMxColPad = 128;   // column-wise MXFP8 groups are padded to this many rows
 
 inline hipStream_t as_stream(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 

@@ -165,11 +165,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4* __restrict
     scales[i] = (uint8_t)(e + 127);
 }
 
-// Column-wise quantiser inside row groups.  Block (cb, L): columns
-// [cb*256, cb*256+256) of the L-th 32-row block in the concatenation of all
-// groups' padded row blocks (device schedule from the group offsets).  Each
-// thread quantises one column over those 32 rows and writes the 32 codes as
-// one 32-byte run of the transposed group layout.
+// Column-wise quantiser inside row groups.  Each group's rows are padded to a
+// multiple of kMxColPad (zero codes) and stored transposed, so that a GEMM
+// over the group reads whole 128-element K-steps and 4-byte scale words.
+// Block (cb, L): columns [cb*256, cb*256+256) of the L-th 32-row block in the
+// concatenation of all groups' padded row blocks (device schedule from the
+// group offsets).  Each thread quantises one column over those 32 rows and
+// writes the 32 codes as one 32-byte run of the transposed group layout.
 template <bool FROM_MX>
 __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restrict__ src,
                                                          const uint8_t* __restrict__ src_codes,
@@ -182,23 +184,24 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
 {
     __shared__ int s_pref[kMaxExperts + 1];
     __shared__ int s_part[256];
+    constexpr int BPP = kMxColPad / 32;   // 32-row blocks per padding unit
     int g = 0, rb = blockIdx.y;
     int64_t g0 = 0, g1 = rows, P = 0;
     if (group_off || capacity > 0) {
-        const int total =
-            block_tile_prefix<256>(group_off, capacity, n_groups, rows, 32, 1, s_pref, s_part);
+        const int total = block_tile_prefix<256>(group_off, capacity, n_groups, rows, kMxColPad,
+                                                 BPP, s_pref, s_part);
         if ((int)blockIdx.y >= total) return;
         g = find_group(s_pref, n_groups, blockIdx.y);
         rb = blockIdx.y - s_pref[g];
         g0 = group_begin(group_off, capacity, g, rows);
         g1 = g0 + group_rows(group_off, capacity, g, rows);
         P = (int64_t)s_pref[g] * 32;              // padded rows of earlier groups
-    } else if ((int64_t)rb * 32 >= rows) {
+    } else if ((int64_t)rb * 32 >= (rows + kMxColPad - 1) / kMxColPad * kMxColPad) {
         return;
     }
     const int c = blockIdx.x * 256 + threadIdx.x;
     if (c >= K) return;
-    const int64_t mpad = (g1 - g0 + 31) / 32 * 32;
+    const int64_t mpad = (g1 - g0 + kMxColPad - 1) / kMxColPad * kMxColPad;
     float vals[32];
     float amax = 0.0f;
 #pragma unroll
@@ -365,8 +368,9 @@ static hipError_t launch_cols(bool from_mx, const uint16_t* src, const uint8_t* 
                               int capacity, int n_groups, uint8_t* codes, uint8_t* scales,
                               hipStream_t s)
 {
-    // bound on the number of 32-row blocks over all groups
-    const int64_t nrb = rows / 32 + (group_off || capacity > 0 ? n_groups : 1);
+    // bound on the number of 32-row blocks over all padded groups
+    const int64_t ngr = group_off || capacity > 0 ? n_groups : 1;
+    const int64_t nrb = (rows + ngr * kMxColPad) / 32;
     if (nrb == 0 || K == 0) return hipGetLastError();
     const dim3 grid((unsigned)((K + 255) / 256), (unsigned)nrb);
     if (from_mx)

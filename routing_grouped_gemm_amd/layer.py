@@ -85,13 +85,16 @@ class MoELayer:
         self.w2_s = torch.empty(E * d, f // 32, **u8)
         moe_quantize_mxfp8(w2.reshape(E * d, f), 0, self.w2_q, self.w2_s)
         # backward direction: each expert's matrix transposed, blocks along 2f / d
+        # (column-wise quantiser layout: K * (rows + 128 * groups) codes)
         g13 = torch.arange(0, E + 1, dtype=torch.int32, device=dev) * (2 * f)
         g2 = torch.arange(0, E + 1, dtype=torch.int32, device=dev) * d
-        self.w13t_q = torch.empty(E * d * 2 * f, **u8)
-        self.w13t_s = torch.empty(E * d * 2 * f // 32, **u8)
+        n13 = d * (E * 2 * f + 128 * E)
+        n2 = f * (E * d + 128 * E)
+        self.w13t_q = torch.empty(n13, **u8)
+        self.w13t_s = torch.empty(n13 // 32, **u8)
         moe_quantize_mxfp8(w13.reshape(E * 2 * f, d), 1, self.w13t_q, self.w13t_s, g13, E)
-        self.w2t_q = torch.empty(E * f * d, **u8)
-        self.w2t_s = torch.empty(E * f * d // 32, **u8)
+        self.w2t_q = torch.empty(n2, **u8)
+        self.w2t_s = torch.empty(n2 // 32, **u8)
         moe_quantize_mxfp8(w2.reshape(E * d, f), 1, self.w2t_q, self.w2t_s, g2, E)
 
     # -------------------------------------------------------------- steps
