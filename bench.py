@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% MFMA peak), E=128 top-4 bf16"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 (and MX-scaled fp8) MFMA
 PEAK_F32_TFLOPS = 157.3         # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 
@@ -40,23 +41,40 @@ KERNEL_NAMES = {
     "permute": "permute_kernel<true, false>",
     "combine": "combine_kernel<true>",
 }
+KERNEL_NAMES_MX = {
+    "gemm_gate_up": "mx_grouped_m_kernel<256, 1> (gate/up + SwiGLU)",
+    "gemm_down": "quant_rows_kernel (h) + mx_grouped_m_kernel<256, 0> (down)",
+    "gemm_dgrad_down": "quant_rows_kernel (dy) + mx_grouped_m_kernel<256, 2> (dgrad down + SwiGLU bwd)",
+    "gemm_dgrad_gate_up": "quant_rows_kernel (dgu) + mx_grouped_m_kernel<256, 0> (dgrad gate/up)",
+    "gemm_wgrad": "4 x quant_cols_kernel + mx_grouped_k_kernel<256> (wgrad, dWd and dW13)",
+    "permute": "permute_mx_kernel",
+    "combine": "combine_kernel<true>",
+}
 
 
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = {"gemm": "routing_grouped_gemm_amd/csrc/gemm_bf16.hip",
-                  "route": "routing_grouped_gemm_amd/csrc/route.hip",
-                  "permute": "routing_grouped_gemm_amd/csrc/permute.hip",
-                  "combine": "routing_grouped_gemm_amd/csrc/permute.hip"}
+_CSRC = "routing_grouped_gemm_amd/csrc/"
+# the sources each stage's kernels are compiled from (a traffic record is
+# only valid for the exact sources it was measured on)
+KERNEL_SOURCES = {"gemm": ["gemm_bf16.hip", "gemm_common.h", "moe_internal.h"],
+                  "gemm_mx": ["gemm_mxfp8.hip", "gemm_common.h", "moe_internal.h", "permute.hip"],
+                  "route": ["route.hip", "moe_internal.h"],
+                  "permute": ["permute.hip", "moe_internal.h"],
+                  "combine": ["permute.hip", "moe_internal.h"]}
 
 
-def source_hash(stage):
+def source_hash(stage, mx=False):
     import hashlib
-    key = "gemm" if stage.startswith("gemm") else stage.split("_")[0]
-    path = os.path.join(ROOT, KERNEL_SOURCES.get(key, KERNEL_SOURCES["gemm"]))
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    key = stage.split("_")[0]
+    if key == "gemm" and mx:
+        key = "gemm_mx"
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES.get(key, KERNEL_SOURCES["permute"]):
+        h.update(open(os.path.join(ROOT, _CSRC, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(stage, workload):
+def measured_traffic(stage, workload, mx=False):
     """HBM bytes per launch of `stage` from the committed counter record
     (profiles/traffic_<stage>_<workload>.json), or None when there is none or
     the kernel source changed since the counters were taken."""
@@ -64,7 +82,7 @@ def measured_traffic(stage, workload):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256_16") != source_hash(stage):
+    if rec.get("source_sha256_16") != source_hash(stage, mx):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -86,10 +104,17 @@ def roofline(attainable_peak, bandwidth, intensity):
     return min(attainable_peak, bandwidth * intensity)
 
 
-def stage_work(name, T, d, E, f, k, R, elem=2):
+MX_ELEM = 1 + 1 / 32             # bytes per MXFP8 element: E4M3 code + its share of the E8M0 scale
+
+
+def stage_work(name, T, d, E, f, k, R, elem=2, mx=False):
     """Algorithmic (FLOPs, HBM bytes) of one stage: useful work only, padding
     rows never counted; bytes = each operand read once and each result
-    written once."""
+    written once.  MXFP8 (mx=True): the dispatch payload and the weights are
+    read as codes + scales, every other activation is bf16 (a stage's own
+    quantisation of a bf16 operand is internal to the stage)."""
+    if mx:
+        return _stage_work_mx(name, T, d, E, f, k, R)
     a = elem
     if name == "route":
         return 0, T * E * 4 + T * k * (4 + 4 + 4) + R * 4 + E * 8
@@ -111,6 +136,22 @@ def stage_work(name, T, d, E, f, k, R, elem=2):
     raise KeyError(name)
 
 
+def _stage_work_mx(name, T, d, E, f, k, R):
+    q, a = MX_ELEM, 2
+    W13, W2 = E * 2 * f * d * q, E * d * f * q
+    if name == "permute":
+        return 0, T * d * a + R * d * q + T * k * 4
+    if name == "gemm_gate_up":
+        return 4 * R * d * f, R * d * q + W13 + R * 3 * f * a
+    if name == "gemm_wgrad":
+        return 6 * R * d * f, R * d * a + R * f * a + R * 2 * f * a + R * d * q + 2 * (W13 + W2) / q
+    if name.startswith("gemm"):
+        fl, by = stage_work(name, T, d, E, f, k, R, 2)
+        return fl, by - (E * 2 * f * d * a if "gate_up" in name else E * d * f * a) + \
+            (W13 if "gate_up" in name else W2)
+    return stage_work(name, T, d, E, f, k, R, 2)
+
+
 def run_gpu(args, cfg):
     import torch
 
@@ -119,7 +160,7 @@ def run_gpu(args, cfg):
     from routing_grouped_gemm_amd.layer import MoELayer
 
     T, d, E, f, k = cfg["T"], cfg["d"], cfg["E"], cfg["f"], cfg["k"]
-    dt = {"bf16": m.MOE_BF16, "f32": m.MOE_F32}[cfg["dtype"]]
+    dt = {"bf16": m.MOE_BF16, "f32": m.MOE_F32, "mxfp8": m.MOE_MXFP8}[cfg["dtype"]]
     cap = 0
     if args.padded:
         cap = moe_synth.capacity_of(T, k, E, cfg.get("capacity_factor", 1.25))
@@ -128,11 +169,10 @@ def run_gpu(args, cfg):
     lay.set_weights(inp["w13"], inp["w2"])
     lay._alloc_bwd()
     R = lay.n_rows
-    act_dt = dt
-    ten = m.gemm_tensors(x_perm=lay.x_perm, w13=lay.w13, w2=lay.w2, gu=lay.gu, h=lay.h,
-                         y_perm=lay.y_perm, dy_perm=lay.dy_perm, dgu=lay.dgu,
-                         dx_perm=lay.dx_perm, dw13=lay.dw13, dw2=lay.dw2)
-    goff = lay.offsets
+    act_dt = m.MOE_F32 if dt == m.MOE_F32 else m.MOE_BF16
+    # combine weights: the router's softmax weights, or the per-row gate a
+    # received expert-parallel shard comes with
+    wts = inp["gate"] if "gate" in inp else lay.topk_w
 
     def step(ev):
         def mark(i):
@@ -143,20 +183,20 @@ def run_gpu(args, cfg):
         mark(1)
         lay.permute(inp["x"])
         mark(2)
-        m.moe_grouped_gemm_op(m.MOE_GEMM_GATE_UP, dt, ten, goff, cap, E, R, d, f)
+        lay.gemm_stage(m.MOE_GEMM_GATE_UP)
         mark(3)
-        m.moe_grouped_gemm_op(m.MOE_GEMM_DOWN, dt, ten, goff, cap, E, R, d, f)
+        lay.gemm_stage(m.MOE_GEMM_DOWN)
         mark(4)
-        lay.combine()
+        lay.combine(wts)
         mark(5)
         m.moe_permute(act_dt, inp["dout"], k, lay.dst_row, lay.dy_perm, src_slot=lay.src_slot,
-                      row_scale=lay.topk_w, dev_err=lay.dev_err)
+                      row_scale=wts, dev_err=lay.dev_err)
         mark(6)
-        m.moe_grouped_gemm_op(m.MOE_GEMM_DGRAD_DOWN, dt, ten, goff, cap, E, R, d, f)
+        lay.gemm_stage(m.MOE_GEMM_DGRAD_DOWN)
         mark(7)
-        m.moe_grouped_gemm_op(m.MOE_GEMM_DGRAD_GATE_UP, dt, ten, goff, cap, E, R, d, f)
+        lay.gemm_stage(m.MOE_GEMM_DGRAD_GATE_UP)
         mark(8)
-        m.moe_grouped_gemm_op(m.MOE_GEMM_WGRAD, dt, ten, goff, cap, E, R, d, f)
+        lay.gemm_stage(m.MOE_GEMM_WGRAD)
         mark(9)
         m.moe_unpermute_combine(act_dt, lay.dx_perm, lay.dst_row, None, k, lay.dx,
                                 dev_err=lay.dev_err)
@@ -187,9 +227,9 @@ def run_gpu(args, cfg):
 
 def cpu_baseline(args, cfg, inp):
     """The oracle, untuned, on a bounded sample: route over all T tokens, then
-    the expert FFN forward + backward for the rows of the first n_exp experts
-    (their rows are gathered like the permute does), time scaled to all R
-    routed rows."""
+    the expert FFN forward + backward for the first cpu_rows rows of the
+    first n_exp experts (gathered like the permute does), time scaled to all
+    R routed rows."""
     import numpy as np
     import torch
 
@@ -204,27 +244,49 @@ def cpu_baseline(args, cfg, inp):
     t_route = time.perf_counter() - t0
     n_exp = max(1, min(E, args.cpu_experts))
     rows_total = int(r["offsets"][-1])
-    lo, hi = int(r["offsets"][0]), int(r["offsets"][n_exp])
+    lo = int(r["offsets"][0])
+    hi = min(int(r["offsets"][n_exp]), lo + args.cpu_rows)
     toks = r["src_slot"][lo:hi] // k
     to64 = lambda t: t.detach().cpu().to(torch.float64).numpy()
     x = to64(inp["x"][torch.from_numpy(toks).long().to(inp["x"].device)])
     dout_rows = to64(inp["dout"][torch.from_numpy(toks).long().to(inp["x"].device)])
-    w = r["topk_w"].reshape(-1)[r["src_slot"][lo:hi]].astype(np.float64)
+    if "gate" in inp:
+        w = inp["gate"].cpu().numpy()[toks].astype(np.float64)
+    else:
+        w = r["topk_w"].reshape(-1)[r["src_slot"][lo:hi]].astype(np.float64)
     w13 = to64(inp["w13"][:n_exp])
     w2 = to64(inp["w2"][:n_exp])
-    go = r["offsets"][:n_exp + 1].astype(np.int32)
+    go = np.minimum(r["offsets"][:n_exp + 1], hi).astype(np.int32)
     rows = hi - lo
-    t1 = time.perf_counter()
-    gu, h, y = oracle.ffn_fwd(x, w13, w2, go, oracle.BF16)
     ident = np.arange(rows, dtype=np.int32)
-    dy = oracle.permute(dout_rows, ident, 1, rows, row_scale=w.astype(np.float32),
-                        round_mode=oracle.BF16)
-    oracle.ffn_bwd(dy, x, gu, h, w13, w2, go, oracle.BF16)
+    mx = cfg["dtype"] == "mxfp8"
+    if mx:   # weight caches are made once per optimizer step, outside the step
+        g13 = np.arange(n_exp + 1, dtype=np.int32) * 2 * f
+        g2 = np.arange(n_exp + 1, dtype=np.int32) * d
+        w13f = oracle.mx_qdq_rows(w13.reshape(-1, d)).reshape(w13.shape)
+        w2f = oracle.mx_qdq_rows(w2.reshape(-1, f)).reshape(w2.shape)
+        w13b = oracle.mx_qdq_cols(w13.reshape(-1, d), g13).reshape(w13.shape)
+        w2b = oracle.mx_qdq_cols(w2.reshape(-1, f), g2).reshape(w2.shape)
+    t1 = time.perf_counter()
+    if mx:
+        xq = oracle.mx_qdq_rows(x)
+        gu, h, y = oracle.ffn_fwd(xq, w13f, w2f, go, oracle.BF16, mx_h=True)
+        dy = oracle.permute(dout_rows, ident, 1, rows, row_scale=w.astype(np.float32),
+                            round_mode=oracle.BF16)
+        oracle.ffn_bwd(oracle.mx_qdq_rows(dy), xq, gu, h, w13f, w2f, go, oracle.BF16,
+                       w2_dgrad=w2b, w13_dgrad=w13b, dy_wgrad=oracle.mx_qdq_cols(dy, go),
+                       h_wgrad=oracle.mx_qdq_cols(h, go), x_wgrad=oracle.mx_qdq_cols(xq, go),
+                       mx_dgu=True)
+    else:
+        gu, h, y = oracle.ffn_fwd(x, w13, w2, go, oracle.BF16)
+        dy = oracle.permute(dout_rows, ident, 1, rows, row_scale=w.astype(np.float32),
+                            round_mode=oracle.BF16)
+        oracle.ffn_bwd(dy, x, gu, h, w13, w2, go, oracle.BF16)
     t_ffn = time.perf_counter() - t1
     t_full = t_route + t_ffn * rows_total / max(rows, 1)
     return {"value": T / t_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": (f"oracle route over all {T} tokens ({t_route:.2f} s) + expert FFN fwd+bwd "
-                       f"for the {rows} rows of experts 0..{n_exp - 1} ({t_ffn:.2f} s), "
+                       f"for the first {rows} rows of experts 0..{n_exp - 1} ({t_ffn:.2f} s), "
                        f"scaled to all {rows_total} routed rows"),
             "sample_seconds": round(t_route + t_ffn, 2)}
 
@@ -239,6 +301,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=1,
                     help="experts whose rows the CPU-oracle sample covers")
+    ap.add_argument("--cpu-rows", type=int, default=512,
+                    help="at most this many of those rows")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 2 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -252,17 +316,15 @@ def main():
 
     import moe_synth
     cfg = moe_synth.WORKLOADS[args.workload]
-    if cfg["dtype"] not in ("bf16", "f32"):
-        print(f"workload {args.workload} ({cfg['dtype']}) is not benchmarked here", file=sys.stderr)
-        sys.exit(2)
     T, d, E, f, k = cfg["T"], cfg["d"], cfg["E"], cfg["f"], cfg["k"]
     res = run_gpu(args, cfg)
     R = res["R"]
-    elem = 2 if cfg["dtype"] == "bf16" else 4
+    mx = cfg["dtype"] == "mxfp8"
+    elem = 4 if cfg["dtype"] == "f32" else 2
     routed = T * k - (0 if not args.padded else int((res["lay"].dst_row < 0).sum().item()))
     stages = {}
     for s in STAGES:
-        fl, by = stage_work(s, T, d, E, f, k, routed, elem)
+        fl, by = stage_work(s, T, d, E, f, k, routed, elem, mx)
         ms = res["stage_ms"][s]
         ent = {"ms": round(ms, 4)}
         if fl:
@@ -272,19 +334,19 @@ def main():
     gemm = [s for s in STAGES if s.startswith("gemm")]
     gemm_ms = sum(res["stage_ms"][s] for s in gemm)
     gemm_flops = 18 * routed * d * f
-    peak = PEAK_BF16_TFLOPS if elem == 2 else PEAK_F32_TFLOPS
+    peak = PEAK_FP8_TFLOPS if mx else (PEAK_BF16_TFLOPS if elem == 2 else PEAK_F32_TFLOPS)
     dom = max(STAGES, key=lambda s: res["stage_ms"][s])
-    fl, by = stage_work(dom, T, d, E, f, k, routed, elem)
+    fl, by = stage_work(dom, T, d, E, f, k, routed, elem, mx)
     dom_ms = res["stage_ms"][dom]
     if fl:
-        rl = {"bound": "mfma" if elem == 2 else "alu", "achieved": round(fl / dom_ms / 1e9, 1),
+        rl = {"bound": "alu" if elem == 4 else "mfma", "achieved": round(fl / dom_ms / 1e9, 1),
               "peak": peak, "unit": "TFLOP/s", "frac": round(fl / dom_ms / 1e9 / peak, 4)}
     else:
         rl = {"bound": "hbm", "achieved": round(by / dom_ms / 1e6, 1), "peak": PEAK_HBM_GBS,
               "unit": "GB/s", "frac": round(by / dom_ms / 1e6 / PEAK_HBM_GBS, 4)}
     rl["attainable"] = round(roofline(peak, PEAK_HBM_GBS / 1e3, fl / by), 1) if fl else None
-    rl.update({"traffic": measured_traffic(dom, args.workload + ("_padded" if args.padded else "")),
-               "kernel": KERNEL_NAMES.get(dom, dom), "stage": dom,
+    rl.update({"traffic": measured_traffic(dom, args.workload + ("_padded" if args.padded else ""), mx),
+               "kernel": (KERNEL_NAMES_MX if mx else KERNEL_NAMES).get(dom, dom), "stage": dom,
                "launch_ms": round(dom_ms, 4), "algorithmic_flops": fl, "algorithmic_bytes": by})
     value = T / (res["ms_per_step"] / 1e3)
     out = {

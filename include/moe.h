@@ -190,7 +190,9 @@ MOE_API int moe_grouped_gemm_bwd(int dtype, const void* dy_perm, const void* x_p
                          int d, int f, void* dgu, void* dx_perm, void* dw13, void* dw2,
                          void* ws, size_t ws_bytes, moe_stream_t stream);
 
-/* The grouped GEMM stages, one kernel launch each (MOE_F32 / MOE_BF16). */
+/* The grouped GEMM stages: one kernel launch each for MOE_F32 / MOE_BF16;
+ * for MOE_MXFP8 the quantisation of the stage's bf16 operands into the
+ * workspace, then one block-scaled GEMM launch. */
 enum moe_gemm_op {
     MOE_GEMM_GATE_UP = 0,        /* gu = x [Wg | Wu]^T, h = silu(g) * u               */
     MOE_GEMM_DOWN = 1,           /* y = h Wd^T                                        */
@@ -200,7 +202,13 @@ enum moe_gemm_op {
 };
 
 /* Operands of the grouped GEMM stages (device pointers; unused ones may be
- * NULL).  Shapes and layouts as in moe_grouped_gemm_fwd / _bwd. */
+ * NULL).  Shapes and layouts as in moe_grouped_gemm_fwd / _bwd.  MOE_MXFP8:
+ * x_perm is codes + x_perm_scales (row-wise, as moe_permute writes them);
+ * w13 / w2 (+ scales) hold the forward-direction caches for GATE_UP / DOWN
+ * and the backward-direction caches for DGRAD_GATE_UP / DGRAD_DOWN; every
+ * other activation is bf16; ws / ws_bytes is a workspace of at least
+ * moe_gemm_workspace_bytes (every stage but GATE_UP writes into it, so
+ * stages sharing one workspace must run in order on one stream). */
 typedef struct moe_gemm_tensors {
     const void* x_perm;          /* [n_rows, d]                     */
     const uint8_t* x_perm_scales;
@@ -216,14 +224,16 @@ typedef struct moe_gemm_tensors {
     void* dx_perm;               /* [n_rows, d]                     */
     void* dw13;                  /* [E, 2f, d]                      */
     void* dw2;                   /* [E, d, f]                       */
+    void* ws;                    /* MOE_MXFP8 workspace             */
+    size_t ws_bytes;
 } moe_gemm_tensors;
 
 /*
  * One stage of the grouped SwiGLU GEMM (the forward and backward calls above
- * are GATE_UP + DOWN and DGRAD_DOWN + DGRAD_GATE_UP + WGRAD).  Exactly one
- * kernel launch for MOE_F32 and MOE_BF16; MOE_MXFP8 returns
- * MOE_EUNSUPPORTED (use the fwd / bwd calls).  Inputs a stage reads must have
- * been produced by the earlier stages on the same stream.
+ * are GATE_UP + DOWN and DGRAD_DOWN + DGRAD_GATE_UP + WGRAD, issued through
+ * this same code).  Inputs a stage reads must have been produced by the
+ * earlier stages on the same stream.  Errors as for the fwd / bwd calls;
+ * MOE_EWORKSPACE when an MXFP8 stage that needs the workspace lacks it.
  */
 MOE_API int moe_grouped_gemm_op(int op, int dtype, const moe_gemm_tensors* t,
                                 const int32_t* group_off, int capacity, int E, int64_t n_rows,

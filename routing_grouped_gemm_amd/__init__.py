@@ -27,12 +27,12 @@ ABI_FUNCTIONS = ("moe_route_workspace_bytes", "moe_route_topk", "moe_permute",
                  "moe_status_string", "moe_version")
 
 GEMM_TENSOR_FIELDS = ("x_perm", "x_perm_scales", "w13", "w13_scales", "w2", "w2_scales", "gu",
-                      "h", "y_perm", "dy_perm", "dgu", "dx_perm", "dw13", "dw2")
+                      "h", "y_perm", "dy_perm", "dgu", "dx_perm", "dw13", "dw2", "ws")
 
 
 class MoeGemmTensors(ctypes.Structure):
     """C struct moe_gemm_tensors (device pointers, NULL where unused)."""
-    _fields_ = [(n, ctypes.c_void_p) for n in GEMM_TENSOR_FIELDS]
+    _fields_ = [(n, ctypes.c_void_p) for n in GEMM_TENSOR_FIELDS] + [("ws_bytes", ctypes.c_size_t)]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
@@ -182,15 +182,19 @@ def moe_grouped_gemm_bwd(dtype, dy_perm, x_perm, gu, h, w13, w2, group_off, capa
 
 
 def gemm_tensors(**tensors):
-    """Build a MoeGemmTensors from keyword tensors (names as in GEMM_TENSOR_FIELDS)."""
+    """Build a MoeGemmTensors from keyword tensors (names as in GEMM_TENSOR_FIELDS;
+    ws is a uint8 workspace tensor whose size becomes ws_bytes)."""
     bad = set(tensors) - set(GEMM_TENSOR_FIELDS)
     if bad:
         raise TypeError(f"unknown operand(s) {sorted(bad)}")
-    return MoeGemmTensors(**{n: _p(t) for n, t in tensors.items()})
+    st = MoeGemmTensors(**{n: _p(t) for n, t in tensors.items()})
+    if tensors.get("ws") is not None:
+        st.ws_bytes = tensors["ws"].numel() * tensors["ws"].element_size()
+    return st
 
 
 def moe_grouped_gemm_op(op, dtype, tensors, group_off, capacity, E, n_rows, d, f, stream=None):
-    """One grouped GEMM stage (one kernel launch); tensors is a MoeGemmTensors."""
+    """One grouped GEMM stage; tensors is a MoeGemmTensors (gemm_tensors())."""
     rc = load().moe_grouped_gemm_op(op, dtype, ctypes.byref(tensors), _p(group_off), capacity, E,
                                     n_rows, d, f, _s(stream))
     _check(rc, "moe_grouped_gemm_op")

@@ -22,8 +22,6 @@
 
 namespace moe {
 
-const bool kMxGemmAvailable = true;
-
 namespace {
 
 using namespace gemm;
@@ -366,113 +364,95 @@ size_t carve(void* ws, int E, int64_t R, int d, int f, MxWs* w)
 
 size_t gemm_ws_mxfp8(int E, int64_t n_rows, int d, int f) { return carve(nullptr, E, n_rows, d, f, nullptr) + 256; }
 
-hipError_t gemm_fwd_mxfp8(const uint8_t* xq, const uint8_t* xs, const uint8_t* w13q,
-                          const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
-                          GroupSpec g, int d, int f, uint16_t* gu, uint16_t* h, uint16_t* y,
-                          void* ws, hipStream_t s)
-{
-    MxWs w;
-    carve(ws, g.E, g.n_rows, d, f, &w);
-    // gate/up with the SwiGLU epilogue
-    MxMParams a{};
-    a.p.group_off = g.group_off;
-    a.p.capacity = g.capacity;
-    a.p.E = g.E;
-    a.p.n_rows = g.n_rows;
-    a.p.N = f;
-    a.p.K = d;
-    a.p.f = f;
-    a.p.ntn = (f + 127) / 128;
-    a.p.C = gu;
-    a.p.ldc = 2 * f;
-    a.p.H = h;
-    a.p.ldh = f;
-    a.Aq = xq;
-    a.As = xs;
-    a.Bq = w13q;
-    a.Bs = w13s;
-    a.sBq = (int64_t)2 * f * d;
-    hipError_t err = launch_mx_m<EPI_SWIGLU_FWD>(a, s);
-    if (err != hipSuccess) return err;
-    // h -> MXFP8 along f, then the down projection
-    err = launch_quantize_rows(h, g.n_rows, f, w.hq, w.hs, s);
-    if (err != hipSuccess) return err;
-    MxMParams b{};
-    b.p.group_off = g.group_off;
-    b.p.capacity = g.capacity;
-    b.p.E = g.E;
-    b.p.n_rows = g.n_rows;
-    b.p.N = d;
-    b.p.K = f;
-    b.p.f = f;
-    b.p.ntn = (d + BN - 1) / BN;
-    b.p.C = y;
-    b.p.ldc = d;
-    b.Aq = w.hq;
-    b.As = w.hs;
-    b.Bq = w2q;
-    b.Bs = w2s;
-    b.sBq = (int64_t)d * f;
-    return launch_mx_m<EPI_STORE>(b, s);
-}
-
-hipError_t gemm_bwd_mxfp8(const uint16_t* dy, const uint8_t* xq, const uint8_t* xs,
-                          const uint16_t* gu, const uint16_t* h, const uint8_t* w13tq,
-                          const uint8_t* w13ts, const uint8_t* w2tq, const uint8_t* w2ts,
-                          GroupSpec g, int d, int f, uint16_t* dgu, uint16_t* dx,
-                          uint16_t* dw13, uint16_t* dw2, void* ws, hipStream_t s)
+// One stage of the MXFP8 grouped GEMM.  Each stage quantises the bf16
+// operands it reads (into the workspace) and then runs one block-scaled GEMM;
+// w13 / w2 are the forward caches for GATE_UP / DOWN and the backward
+// (transposed, column-quantised) caches for the two DGRAD stages.
+hipError_t gemm_op_mxfp8(int op, const moe_gemm_tensors& t, GroupSpec g, int d, int f, void* ws,
+                         hipStream_t s)
 {
     MxWs w;
     carve(ws, g.E, g.n_rows, d, f, &w);
     const int64_t R = g.n_rows;
-    hipError_t err = launch_quantize_rows(dy, R, d, w.dyq, w.dys, s);
-    if (err != hipSuccess) return err;
-    // dh = dy Wd (backward cache Wd^T [E, f, d]) with the SwiGLU backward
+    hipError_t err = hipSuccess;
     MxMParams a{};
     a.p.group_off = g.group_off;
     a.p.capacity = g.capacity;
     a.p.E = g.E;
     a.p.n_rows = R;
-    a.p.N = f;
-    a.p.K = d;
     a.p.f = f;
-    a.p.ntn = (f + BN - 1) / BN;
-    a.p.C = dgu;
-    a.p.ldc = 2 * f;
-    a.p.G = gu;
-    a.p.ldg = 2 * f;
-    a.Aq = w.dyq;
-    a.As = w.dys;
-    a.Bq = w2tq;
-    a.Bs = w2ts;
-    a.sBq = (int64_t)f * d;
-    if ((err = launch_mx_m<EPI_SWIGLU_BWD>(a, s)) != hipSuccess) return err;
-    // dx = [dg | du] [Wg ; Wu]  (backward cache W13^T [E, d, 2f])
-    if ((err = launch_quantize_rows(dgu, R, 2 * f, w.dguq, w.dgus, s)) != hipSuccess) return err;
-    MxMParams b{};
-    b.p.group_off = g.group_off;
-    b.p.capacity = g.capacity;
-    b.p.E = g.E;
-    b.p.n_rows = R;
-    b.p.N = d;
-    b.p.K = 2 * f;
-    b.p.f = f;
-    b.p.ntn = (d + BN - 1) / BN;
-    b.p.C = dx;
-    b.p.ldc = d;
-    b.Aq = w.dguq;
-    b.As = w.dgus;
-    b.Bq = w13tq;
-    b.Bs = w13ts;
-    b.sBq = (int64_t)d * 2 * f;
-    if ((err = launch_mx_m<EPI_STORE>(b, s)) != hipSuccess) return err;
-    // weight-gradient operands: column-wise inside each expert's rows
-    if ((err = launch_quantize_cols(dy, R, d, g.group_off, g.capacity, g.E, w.dyT, w.dyTs, s)) != hipSuccess) return err;
-    if ((err = launch_quantize_cols(h, R, f, g.group_off, g.capacity, g.E, w.hT, w.hTs, s)) != hipSuccess) return err;
-    if ((err = launch_quantize_cols(dgu, R, 2 * f, g.group_off, g.capacity, g.E, w.dguT, w.dguTs, s)) != hipSuccess)
+    a.Bq = static_cast<const uint8_t*>(op == MOE_GEMM_GATE_UP || op == MOE_GEMM_DGRAD_GATE_UP ? t.w13 : t.w2);
+    a.Bs = op == MOE_GEMM_GATE_UP || op == MOE_GEMM_DGRAD_GATE_UP ? t.w13_scales : t.w2_scales;
+    switch (op) {
+    case MOE_GEMM_GATE_UP:   // gu = x [Wg | Wu]^T with the SwiGLU epilogue
+        a.p.N = f;
+        a.p.K = d;
+        a.p.ntn = (f + 127) / 128;
+        a.p.C = static_cast<uint16_t*>(t.gu);
+        a.p.ldc = 2 * f;
+        a.p.H = static_cast<uint16_t*>(t.h);
+        a.p.ldh = f;
+        a.Aq = static_cast<const uint8_t*>(t.x_perm);
+        a.As = t.x_perm_scales;
+        a.sBq = (int64_t)2 * f * d;
+        return launch_mx_m<EPI_SWIGLU_FWD>(a, s);
+    case MOE_GEMM_DOWN:      // y = h Wd^T, h quantised along f
+        if ((err = launch_quantize_rows(static_cast<const uint16_t*>(t.h), R, f, w.hq, w.hs, s)) != hipSuccess)
+            return err;
+        a.p.N = d;
+        a.p.K = f;
+        a.p.ntn = (d + BN - 1) / BN;
+        a.p.C = static_cast<uint16_t*>(t.y_perm);
+        a.p.ldc = d;
+        a.Aq = w.hq;
+        a.As = w.hs;
+        a.sBq = (int64_t)d * f;
+        return launch_mx_m<EPI_STORE>(a, s);
+    case MOE_GEMM_DGRAD_DOWN:   // dh = dy Wd (cache Wd^T [E, f, d]) with the SwiGLU backward
+        if ((err = launch_quantize_rows(static_cast<const uint16_t*>(t.dy_perm), R, d, w.dyq, w.dys, s)) !=
+            hipSuccess)
+            return err;
+        a.p.N = f;
+        a.p.K = d;
+        a.p.ntn = (f + BN - 1) / BN;
+        a.p.C = static_cast<uint16_t*>(t.dgu);
+        a.p.ldc = 2 * f;
+        a.p.G = static_cast<const uint16_t*>(t.gu);
+        a.p.ldg = 2 * f;
+        a.Aq = w.dyq;
+        a.As = w.dys;
+        a.sBq = (int64_t)f * d;
+        return launch_mx_m<EPI_SWIGLU_BWD>(a, s);
+    case MOE_GEMM_DGRAD_GATE_UP:   // dx = [dg | du] [Wg ; Wu] (cache W13^T [E, d, 2f])
+        if ((err = launch_quantize_rows(static_cast<const uint16_t*>(t.dgu), R, 2 * f, w.dguq, w.dgus, s)) !=
+            hipSuccess)
+            return err;
+        a.p.N = d;
+        a.p.K = 2 * f;
+        a.p.ntn = (d + BN - 1) / BN;
+        a.p.C = static_cast<uint16_t*>(t.dx_perm);
+        a.p.ldc = d;
+        a.Aq = w.dguq;
+        a.As = w.dgus;
+        a.sBq = (int64_t)d * 2 * f;
+        return launch_mx_m<EPI_STORE>(a, s);
+    case MOE_GEMM_WGRAD:
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    // weight gradients: all four operands column-wise inside each expert's rows
+    const uint16_t* dy = static_cast<const uint16_t*>(t.dy_perm);
+    if ((err = launch_quantize_cols(dy, R, d, g.group_off, g.capacity, g.E, w.dyT, w.dyTs, s)) != hipSuccess)
         return err;
-    if ((err = launch_dequant_requant_cols(xq, xs, R, d, g.group_off, g.capacity, g.E, w.xT, w.xTs, s)) !=
-        hipSuccess)
+    if ((err = launch_quantize_cols(static_cast<const uint16_t*>(t.h), R, f, g.group_off, g.capacity, g.E, w.hT,
+                                    w.hTs, s)) != hipSuccess)
+        return err;
+    if ((err = launch_quantize_cols(static_cast<const uint16_t*>(t.dgu), R, 2 * f, g.group_off, g.capacity, g.E,
+                                    w.dguT, w.dguTs, s)) != hipSuccess)
+        return err;
+    if ((err = launch_dequant_requant_cols(static_cast<const uint8_t*>(t.x_perm), t.x_perm_scales, R, d,
+                                           g.group_off, g.capacity, g.E, w.xT, w.xTs, s)) != hipSuccess)
         return err;
     MxKParams k{};
     k.group_off = g.group_off;
@@ -488,7 +468,7 @@ hipError_t gemm_bwd_mxfp8(const uint16_t* dy, const uint8_t* xq, const uint8_t* 
     p0.N = f;
     p0.mtn = (d + kMxBM - 1) / kMxBM;
     p0.ntn = (f + BN - 1) / BN;
-    p0.C = dw2;
+    p0.C = static_cast<uint16_t*>(t.dw2);
     p0.ldc = f;
     p0.sC = (int64_t)d * f;
     MxKProblem& p1 = k.pr[1];   // dW13 [2f, d] = dgu^T x
@@ -500,7 +480,7 @@ hipError_t gemm_bwd_mxfp8(const uint16_t* dy, const uint8_t* xq, const uint8_t* 
     p1.N = d;
     p1.mtn = (2 * f + kMxBM - 1) / kMxBM;
     p1.ntn = (d + BN - 1) / BN;
-    p1.C = dw13;
+    p1.C = static_cast<uint16_t*>(t.dw13);
     p1.ldc = d;
     p1.sC = (int64_t)2 * f * d;
     const int64_t total = (int64_t)g.E * (p0.mtn * p0.ntn + p1.mtn * p1.ntn);

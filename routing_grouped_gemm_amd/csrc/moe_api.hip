@@ -34,6 +34,17 @@ int check_gemm_shape(int dtype, const int32_t* group_off, int capacity, int E, i
     return MOE_OK;
 }
 
+// one grouped GEMM stage in the given arithmetic
+int run_gemm_op(int op, int dtype, const moe_gemm_tensors& t, const GroupSpec& g, int d, int f,
+                hipStream_t s)
+{
+    hipError_t e;
+    if (dtype == MOE_F32) e = gemm_op_f32(op, t, g, d, f, s);
+    else if (dtype == MOE_BF16) e = gemm_op_bf16(op, t, g, d, f, s);
+    else e = gemm_op_mxfp8(op, t, g, d, f, t.ws, s);
+    return status_of(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -142,30 +153,29 @@ int moe_grouped_gemm_fwd(int dtype, const void* x_perm, const uint8_t* x_perm_sc
     if (n_rows > 0 && (!x_perm || !gu || !h || !y_perm)) return MOE_EINVAL;
     for (const void* p : {x_perm, w13, w2, (const void*)gu, (const void*)h, (const void*)y_perm})
         if (!aligned16(p)) return MOE_EALIGN;
-    GroupSpec g{capacity > 0 ? nullptr : group_off, capacity, E, n_rows};
-    hipStream_t s = as_stream(stream);
-    if (dtype != MOE_MXFP8) {
-        moe_gemm_tensors t{};
-        t.x_perm = x_perm;
-        t.w13 = w13;
-        t.w2 = w2;
-        t.gu = gu;
-        t.h = h;
-        t.y_perm = y_perm;
-        for (int op : {MOE_GEMM_GATE_UP, MOE_GEMM_DOWN}) {
-            const hipError_t e = dtype == MOE_F32 ? gemm_op_f32(op, t, g, d, f, s)
-                                                  : gemm_op_bf16(op, t, g, d, f, s);
-            if (e != hipSuccess) return MOE_EHIP;
-        }
-        return MOE_OK;
+    if (dtype == MOE_MXFP8) {
+        if (!x_perm_scales || !w13_scales || !w2_scales) return MOE_EINVAL;
+        if (!ws || ws_bytes < moe_gemm_workspace_bytes(dtype, E, n_rows, d, f) || !aligned16(ws))
+            return MOE_EWORKSPACE;
     }
-    if (!x_perm_scales || !w13_scales || !w2_scales) return MOE_EINVAL;
-    const size_t need = moe_gemm_workspace_bytes(dtype, E, n_rows, d, f);
-    if (!ws || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
-    if (!kMxGemmAvailable) return MOE_EUNSUPPORTED;
-    return status_of(gemm_fwd_mxfp8((const uint8_t*)x_perm, x_perm_scales, (const uint8_t*)w13,
-                                    w13_scales, (const uint8_t*)w2, w2_scales, g, d, f,
-                                    (uint16_t*)gu, (uint16_t*)h, (uint16_t*)y_perm, ws, s));
+    moe_gemm_tensors t{};
+    t.x_perm = x_perm;
+    t.x_perm_scales = x_perm_scales;
+    t.w13 = w13;
+    t.w13_scales = w13_scales;
+    t.w2 = w2;
+    t.w2_scales = w2_scales;
+    t.gu = gu;
+    t.h = h;
+    t.y_perm = y_perm;
+    t.ws = ws;
+    t.ws_bytes = ws_bytes;
+    const GroupSpec g{capacity > 0 ? nullptr : group_off, capacity, E, n_rows};
+    for (int op : {MOE_GEMM_GATE_UP, MOE_GEMM_DOWN}) {
+        const int st2 = run_gemm_op(op, dtype, t, g, d, f, as_stream(stream));
+        if (st2 != MOE_OK) return st2;
+    }
+    return MOE_OK;
 }
 
 int moe_grouped_gemm_bwd(int dtype, const void* dy_perm, const void* x_perm,
@@ -182,36 +192,33 @@ int moe_grouped_gemm_bwd(int dtype, const void* dy_perm, const void* x_perm,
     for (const void* p : {dy_perm, x_perm, gu, h, w13, w2, (const void*)dgu, (const void*)dx_perm,
                           (const void*)dw13, (const void*)dw2})
         if (!aligned16(p)) return MOE_EALIGN;
-    GroupSpec g{capacity > 0 ? nullptr : group_off, capacity, E, n_rows};
-    hipStream_t s = as_stream(stream);
-    if (dtype != MOE_MXFP8) {
-        moe_gemm_tensors t{};
-        t.x_perm = x_perm;
-        t.w13 = w13;
-        t.w2 = w2;
-        t.gu = const_cast<void*>(gu);
-        t.h = const_cast<void*>(h);
-        t.dy_perm = dy_perm;
-        t.dgu = dgu;
-        t.dx_perm = dx_perm;
-        t.dw13 = dw13;
-        t.dw2 = dw2;
-        for (int op : {MOE_GEMM_DGRAD_DOWN, MOE_GEMM_DGRAD_GATE_UP, MOE_GEMM_WGRAD}) {
-            const hipError_t e = dtype == MOE_F32 ? gemm_op_f32(op, t, g, d, f, s)
-                                                  : gemm_op_bf16(op, t, g, d, f, s);
-            if (e != hipSuccess) return MOE_EHIP;
-        }
-        return MOE_OK;
+    if (dtype == MOE_MXFP8) {
+        if (!x_perm_scales || !w13_scales || !w2_scales) return MOE_EINVAL;
+        if (!ws || ws_bytes < moe_gemm_workspace_bytes(dtype, E, n_rows, d, f) || !aligned16(ws))
+            return MOE_EWORKSPACE;
     }
-    if (!x_perm_scales || !w13_scales || !w2_scales) return MOE_EINVAL;
-    const size_t need = moe_gemm_workspace_bytes(dtype, E, n_rows, d, f);
-    if (!ws || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
-    if (!kMxGemmAvailable) return MOE_EUNSUPPORTED;
-    return status_of(gemm_bwd_mxfp8((const uint16_t*)dy_perm, (const uint8_t*)x_perm,
-                                    x_perm_scales, (const uint16_t*)gu, (const uint16_t*)h,
-                                    (const uint8_t*)w13, w13_scales, (const uint8_t*)w2,
-                                    w2_scales, g, d, f, (uint16_t*)dgu, (uint16_t*)dx_perm,
-                                    (uint16_t*)dw13, (uint16_t*)dw2, ws, s));
+    moe_gemm_tensors t{};
+    t.x_perm = x_perm;
+    t.x_perm_scales = x_perm_scales;
+    t.w13 = w13;
+    t.w13_scales = w13_scales;
+    t.w2 = w2;
+    t.w2_scales = w2_scales;
+    t.gu = const_cast<void*>(gu);
+    t.h = const_cast<void*>(h);
+    t.dy_perm = dy_perm;
+    t.dgu = dgu;
+    t.dx_perm = dx_perm;
+    t.dw13 = dw13;
+    t.dw2 = dw2;
+    t.ws = ws;
+    t.ws_bytes = ws_bytes;
+    const GroupSpec g{capacity > 0 ? nullptr : group_off, capacity, E, n_rows};
+    for (int op : {MOE_GEMM_DGRAD_DOWN, MOE_GEMM_DGRAD_GATE_UP, MOE_GEMM_WGRAD}) {
+        const int st2 = run_gemm_op(op, dtype, t, g, d, f, as_stream(stream));
+        if (st2 != MOE_OK) return st2;
+    }
+    return MOE_OK;
 }
 
 int moe_grouped_gemm_op(int op, int dtype, const moe_gemm_tensors* t,
@@ -220,9 +227,18 @@ int moe_grouped_gemm_op(int op, int dtype, const moe_gemm_tensors* t,
 {
     if (!t) return MOE_EINVAL;
     if (op < MOE_GEMM_GATE_UP || op > MOE_GEMM_WGRAD) return MOE_EINVAL;
-    if (dtype == MOE_MXFP8) return MOE_EUNSUPPORTED;
     int st = check_gemm_shape(dtype, group_off, capacity, E, n_rows, d, f);
     if (st != MOE_OK) return st;
+    if (dtype == MOE_MXFP8) {
+        const bool w13_op = op == MOE_GEMM_GATE_UP || op == MOE_GEMM_DGRAD_GATE_UP;
+        const bool w2_op = op == MOE_GEMM_DOWN || op == MOE_GEMM_DGRAD_DOWN;
+        if ((w13_op && !t->w13_scales) || (w2_op && !t->w2_scales)) return MOE_EINVAL;
+        if ((op == MOE_GEMM_GATE_UP || op == MOE_GEMM_WGRAD) && n_rows > 0 && !t->x_perm_scales)
+            return MOE_EINVAL;
+        if (op != MOE_GEMM_GATE_UP &&
+            (!t->ws || t->ws_bytes < moe_gemm_workspace_bytes(dtype, E, n_rows, d, f) || !aligned16(t->ws)))
+            return MOE_EWORKSPACE;
+    }
     // operands each stage reads (r) and writes (w)
     const void* need[4] = {nullptr, nullptr, nullptr, nullptr};
     int n = 0;
@@ -246,11 +262,8 @@ int moe_grouped_gemm_op(int op, int dtype, const moe_gemm_tensors* t,
             if (!aligned16(need[i])) return MOE_EALIGN;
         }
     }
-    GroupSpec g{capacity > 0 ? nullptr : group_off, capacity, E, n_rows};
-    hipStream_t s = as_stream(stream);
-    const hipError_t e = dtype == MOE_F32 ? gemm_op_f32(op, *t, g, d, f, s)
-                                          : gemm_op_bf16(op, *t, g, d, f, s);
-    return status_of(e);
+    const GroupSpec g{capacity > 0 ? nullptr : group_off, capacity, E, n_rows};
+    return run_gemm_op(op, dtype, *t, g, d, f, as_stream(stream));
 }
 
 int moe_quantize_mxfp8(const void* src, int64_t rows, int K, int colwise, const int32_t* group_off,

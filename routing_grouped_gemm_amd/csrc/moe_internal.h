@@ -169,16 +169,8 @@ hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, i
                         hipStream_t s);
 hipError_t gemm_op_f32(int op, const moe_gemm_tensors& t, GroupSpec g, int d, int f,
                        hipStream_t s);
-extern const bool kMxGemmAvailable;  // false until the MXFP8 GEMMs are provided
 size_t gemm_ws_mxfp8(int E, int64_t n_rows, int d, int f);
-hipError_t gemm_fwd_mxfp8(const uint8_t* xq, const uint8_t* xs, const uint8_t* w13q,
-                          const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
-                          GroupSpec g, int d, int f, uint16_t* gu, uint16_t* h, uint16_t* y,
-                          void* ws, hipStream_t s);
-hipError_t gemm_bwd_mxfp8(const uint16_t* dy, const uint8_t* xq, const uint8_t* xs,
-                          const uint16_t* gu, const uint16_t* h, const uint8_t* w13q,
-                          const uint8_t* w13s, const uint8_t* w2q, const uint8_t* w2s,
-                          GroupSpec g, int d, int f, uint16_t* dgu, uint16_t* dx,
-                          uint16_t* dw13, uint16_t* dw2, void* ws, hipStream_t s);
+hipError_t gemm_op_mxfp8(int op, const moe_gemm_tensors& t, GroupSpec g, int d, int f, void* ws,
+                         hipStream_t s);
 
 }  // namespace moe

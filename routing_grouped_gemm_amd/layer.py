@@ -13,8 +13,9 @@ The backward of the layer with the routing held fixed:
 """
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_MXFP8, moe_gemm_workspace_bytes, moe_grouped_gemm_bwd,
-               moe_grouped_gemm_fwd, moe_permute, moe_quantize_mxfp8, moe_route_topk,
+from . import (MOE_BF16, MOE_F32, MOE_GEMM_DGRAD_DOWN, MOE_GEMM_DGRAD_GATE_UP, MOE_MXFP8,
+               gemm_tensors, moe_gemm_workspace_bytes, moe_grouped_gemm_bwd, moe_grouped_gemm_fwd,
+               moe_grouped_gemm_op, moe_permute, moe_quantize_mxfp8, moe_route_topk,
                moe_route_workspace_bytes, moe_unpermute_combine)
 
 _ACT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_MXFP8: torch.bfloat16}
@@ -72,6 +73,7 @@ class MoELayer:
         """Weights [E, 2f, d] and [E, d, f] (fp32 or bf16).  For MXFP8 the forward
         and backward MXFP8 caches are made here (once per optimizer step)."""
         self.w13, self.w2 = w13, w2
+        self._stages = None
         if self.dtype != MOE_MXFP8:
             return
         E, f, d = self.E, self.f, self.d
@@ -96,6 +98,33 @@ class MoELayer:
         self.w2t_q = torch.empty(n2, **u8)
         self.w2t_s = torch.empty(n2 // 32, **u8)
         moe_quantize_mxfp8(w2.reshape(E * d, f), 1, self.w2t_q, self.w2t_s, g2, E)
+
+    # -------------------------------------------------------------- stages
+    def _stage_tensors(self):
+        """Operands of the five grouped GEMM stages: (forward-direction set,
+        backward-direction set); they differ only in the MXFP8 weight caches."""
+        self._alloc_bwd()
+        common = dict(x_perm=self.x_perm, x_perm_scales=self.x_perm_scales, gu=self.gu, h=self.h,
+                      y_perm=self.y_perm, dy_perm=self.dy_perm, dgu=self.dgu, dx_perm=self.dx_perm,
+                      dw13=self.dw13, dw2=self.dw2, ws=self.gemm_ws)
+        if self.dtype != MOE_MXFP8:
+            t = gemm_tensors(w13=self.w13, w2=self.w2, **common)
+            return t, t
+        fwd = gemm_tensors(w13=self.w13_q, w13_scales=self.w13_s, w2=self.w2_q,
+                           w2_scales=self.w2_s, **common)
+        bwd = gemm_tensors(w13=self.w13t_q, w13_scales=self.w13t_s, w2=self.w2t_q,
+                           w2_scales=self.w2t_s, **common)
+        return fwd, bwd
+
+    def gemm_stage(self, op):
+        """Issue one grouped GEMM stage (MOE_GEMM_*) on the layer's buffers (the
+        forward and backward calls are these stages in order).  Call
+        set_weights first; the tensors are bound on first use."""
+        if getattr(self, "_stages", None) is None:
+            self._stages = self._stage_tensors()
+        bwd = op in (MOE_GEMM_DGRAD_DOWN, MOE_GEMM_DGRAD_GATE_UP)
+        moe_grouped_gemm_op(op, self.dtype, self._stages[1 if bwd else 0], self.offsets,
+                            self.capacity, self.E, self.n_rows, self.d, self.f)
 
     # -------------------------------------------------------------- steps
     def route(self, logits):

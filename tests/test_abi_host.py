@@ -137,6 +137,38 @@ def test_gemm_validation(m):
     assert fwd(dtype=m.MOE_MXFP8, xs=P, ws=None) == m.MOE_EWORKSPACE
     assert lib.moe_grouped_gemm_bwd(m.MOE_BF16, P, P, None, P, P, P, None, P, None, P, 0, 8, 100,
                                     128, 128, P, P, None, P, None, 0, None) == m.MOE_EINVAL
+    # one MXFP8 stage: scales of the operands it reads, and the workspace for
+    # every stage but GATE_UP (which reads only the dispatch payload and weights)
+    t = m.MoeGemmTensors(**{n: P for n in m.GEMM_TENSOR_FIELDS})
+    t.ws = None
+
+    def op(o, t=t):
+        return lib.moe_grouped_gemm_op(o, m.MOE_MXFP8, ctypes.byref(t), P, 0, 8, 100, 128, 128, None)
+    for o in (m.MOE_GEMM_DOWN, m.MOE_GEMM_DGRAD_DOWN, m.MOE_GEMM_DGRAD_GATE_UP, m.MOE_GEMM_WGRAD):
+        assert op(o) == m.MOE_EWORKSPACE
+    t.ws, t.ws_bytes = P, lib.moe_gemm_workspace_bytes(m.MOE_MXFP8, 8, 100, 128, 128) - 1
+    assert op(m.MOE_GEMM_DOWN) == m.MOE_EWORKSPACE
+    t.w13_scales = None
+    assert op(m.MOE_GEMM_GATE_UP) == m.MOE_EINVAL
+    assert op(m.MOE_GEMM_DGRAD_GATE_UP) == m.MOE_EINVAL
+    assert op(7) == m.MOE_EINVAL
     assert lib.moe_quantize_mxfp8(P, 10, 48, 0, None, 0, P, P, None) == m.MOE_EALIGN
     assert lib.moe_quantize_mxfp8(P, -1, 64, 0, None, 0, P, P, None) == m.MOE_EINVAL
     assert lib.moe_quantize_mxfp8(P, 10, 64, 1, P, 0, P, P, None) == m.MOE_EINVAL
+
+
+def test_gemm_tensors_struct_matches_header(m, tmp_path):
+    """The ctypes mirror of moe_gemm_tensors has the C struct's size and offsets."""
+    fields = list(m.GEMM_TENSOR_FIELDS) + ["ws_bytes"]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\nint main(void){\n'
+                   '  printf("%zu\\n", sizeof(moe_gemm_tensors));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(moe_gemm_tensors, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(m.MoeGemmTensors)
+    assert got[1:] == [getattr(m.MoeGemmTensors, f).offset for f in fields]

@@ -47,3 +47,17 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_stage_work_mx_counts_codes_and_scales():
+    T, d, E, f, k = 32768, 4096, 16, 1536, 1
+    R = T * k
+    gemm = [s for s in bench.STAGES if s.startswith("gemm")]
+    assert sum(bench.stage_work(s, T, d, E, f, k, R, mx=True)[0] for s in gemm) == 18 * R * d * f
+    # MXFP8 payload: one code byte plus one scale byte per 32 elements
+    assert bench.stage_work("permute", T, d, E, f, k, R, mx=True)[1] == \
+        T * d * 2 + R * d * 33 / 32 + T * k * 4
+    bf, mx = (bench.stage_work("gemm_gate_up", T, d, E, f, k, R, mx=m)[1] for m in (False, True))
+    assert bf - mx == (R * d + E * 2 * f * d) * (2 - 33 / 32)
+    # the bf16 and MXFP8 GEMMs are different kernels: their traffic records differ
+    assert bench.source_hash("gemm_wgrad") != bench.source_hash("gemm_wgrad", mx=True)

@@ -15,7 +15,7 @@ sub-problems that are exact by definition:
     dgu[:, n] for every row of the expert and dWd[:, n], dWg[n, :],
     dWu[n, :] exactly as the full problem defines them.
 Tolerance: max|gpu - ref| <= 2e-2 * max|ref| per tensor (bf16 storage, fp32
-accumulate).
+accumulate); 6e-2 for the MXFP8 shard.
 """
 import sys
 
@@ -181,3 +181,104 @@ def test_fullsize_layer(moe, name, padded):
     tt = torch.from_numpy(t_sel).long().cuda()
     assert_close(np64(lay.out[tt]), np.stack(out_ref), BF16_TOL, f"{name}:out")
     assert_close(np64(lay.dx[tt]), np.stack(dx_ref), BF16_TOL, f"{name}:dx")
+
+
+MX_TOL = 6e-2
+
+
+def test_fullsize_mx_shard(moe):
+    """The MXFP8 expert-parallel shard (32768 received rows, 16 local experts,
+    k=1 with a per-row gate) at full size.  Every GEMM operand is taken
+    through the MXFP8 quantiser in the direction its GEMM contracts over, so
+    the sub-problems below are exact: row-wise quantisation only involves a
+    row, column-wise only a column of one expert's rows."""
+    from routing_grouped_gemm_amd.layer import MoELayer
+    name = "mx_shard"
+    _say(name)
+    cfg = moe_synth.WORKLOADS[name]
+    T, d, E, f, k = cfg["T"], cfg["d"], cfg["E"], cfg["f"], cfg["k"]
+    inp = moe_synth.make_inputs(name, device="cuda")
+    lay = MoELayer(T, d, E, f, k, moe.MOE_MXFP8)
+    lay.set_weights(inp["w13"], inp["w2"])
+    lay.forward(inp["logits"], inp["x"], weights=inp["gate"])
+    lay.backward(inp["dout"], weights=inp["gate"])
+    torch.cuda.synchronize()
+    assert int(lay.dev_err.item()) == 0
+    r = oracle.route(inp["logits"].cpu().numpy(), k)
+    np.testing.assert_array_equal(lay.dst_row.cpu().numpy(), r["dst_row"])
+    np.testing.assert_array_equal(lay.offsets.cpu().numpy(), r["offsets"])
+    np.testing.assert_array_equal(lay.src_slot.cpu().numpy(), r["src_slot"])
+    go = r["offsets"].astype(np.int32)
+    src = r["src_slot"]
+    gate = inp["gate"].cpu().numpy()
+    rng = np.random.default_rng(4242)
+    rows = _sample_rows(go, rng)
+    row_expert = np.searchsorted(go, rows, side="right") - 1
+    x64 = np64(inp["x"].cpu())
+    dout64 = np64(inp["dout"].cpu())
+
+    # ---- dispatch payload: codes and scales of sampled rows, bit-exact
+    idx = torch.tensor(rows, device="cuda")
+    rc, rs = oracle.mx_quantize_rows(x64[src[rows] // k])
+    np.testing.assert_array_equal(lay.x_perm[idx].cpu().numpy(), rc)
+    np.testing.assert_array_equal(lay.x_perm_scales[idx].cpu().numpy(), rs)
+
+    caches = {}
+
+    def cache(e):   # forward (blocks along the input dim) and backward (along the output dim)
+        if e not in caches:
+            w13 = np64(inp["w13"][e].cpu())
+            w2 = np64(inp["w2"][e].cpu())
+            caches[e] = (oracle.mx_qdq_rows(w13), oracle.mx_qdq_rows(w2),
+                         oracle.mx_qdq_cols(w13, np.array([0, 2 * f], np.int32)),
+                         oracle.mx_qdq_cols(w2, np.array([0, d], np.int32)))
+        return caches[e]
+
+    # ---- one-row problems for the sampled rows
+    ref = {n: [] for n in ("gu", "h", "y", "dy", "dgu", "dx", "out")}
+    g1 = np.array([0, 1], np.int32)
+    for r_i, e in zip(rows, row_expert):
+        t = src[r_i] // k
+        w13f, w2f, w13b, w2b = cache(int(e))
+        xq = oracle.mx_qdq_rows(x64[t:t + 1])
+        gu, h, y = oracle.ffn_fwd(xq, w13f[None], w2f[None], g1, oracle.BF16, mx_h=True)
+        dy = oracle.permute(dout64[t:t + 1], np.array([0], np.int32), 1, 1,
+                            row_scale=gate[t:t + 1], round_mode=oracle.BF16)
+        dgu, dxp, _, _ = oracle.ffn_bwd(oracle.mx_qdq_rows(dy), xq, gu, h, w13f[None], w2f[None], g1,
+                                        oracle.BF16, w2_dgrad=w2b[None], w13_dgrad=w13b[None],
+                                        mx_dgu=True)
+        out = oracle.combine(y, np.array([0], np.int32), gate[t:t + 1], 1, 1, oracle.BF16)
+        for n, v in (("gu", gu), ("h", h), ("y", y), ("dy", dy), ("dgu", dgu), ("dx", dxp),
+                     ("out", out)):
+            ref[n].append(v[0])
+    toks = torch.from_numpy(src[rows] // k).long().cuda()
+    for n, t in (("gu", lay.gu[idx]), ("h", lay.h[idx]), ("y", lay.y_perm[idx]),
+                 ("dgu", lay.dgu[idx]), ("dx", lay.dx_perm[idx]), ("out", lay.out[toks])):
+        assert_close(np64(t), np.stack(ref[n]), MX_TOL, f"{name}:{n} rows")
+    assert_close(np64(lay.dy_perm[idx]), np.stack(ref["dy"]), BF16_TOL, f"{name}:dy rows")
+    assert_close(np64(lay.dx[toks]), np.stack(ref["dx"]), MX_TOL, f"{name}:dx tokens")
+
+    # ---- sampled experts and columns: weight gradients over whole groups
+    counts = np.diff(go)
+    n_sel = np.array(sorted(set([0, f - 1] + list(rng.integers(0, f, size=6)))))
+    cols = np.concatenate([n_sel, f + n_sel])
+    for e in (int(np.argmax(counts)), int(np.argmin(counts))):
+        g0, g1e = int(go[e]), int(go[e + 1])
+        m = g1e - g0
+        tok = src[g0:g1e] // k
+        w13f, w2f, w13b, w2b = cache(e)
+        gs = np.array([0, m], np.int32)
+        xq = oracle.mx_qdq_rows(x64[tok])
+        dye = oracle.permute(dout64[tok], np.arange(m, dtype=np.int32), 1, m,
+                             row_scale=gate[tok], round_mode=oracle.BF16)
+        gu_s, h_s, _ = oracle.ffn_fwd(xq, w13f[cols][None], w2f[:, n_sel][None], gs, oracle.BF16)
+        dgu_s, _, dw13_s, dw2_s = oracle.ffn_bwd(
+            oracle.mx_qdq_rows(dye), xq, gu_s, h_s, w13f[cols][None], w2f[:, n_sel][None], gs,
+            oracle.BF16, w2_dgrad=w2b[:, n_sel][None], w13_dgrad=w13b[cols][None],
+            dy_wgrad=oracle.mx_qdq_cols(dye, gs), h_wgrad=oracle.mx_qdq_cols(h_s, gs),
+            x_wgrad=oracle.mx_qdq_cols(xq, gs), mx_dgu=True)
+        assert_close(np64(lay.gu[g0:g1e].cpu())[:, cols], gu_s, MX_TOL, f"{name}:gu expert {e}")
+        assert_close(np64(lay.h[g0:g1e].cpu())[:, n_sel], h_s, MX_TOL, f"{name}:h expert {e}")
+        assert_close(np64(lay.dgu[g0:g1e].cpu())[:, cols], dgu_s, MX_TOL, f"{name}:dgu expert {e}")
+        assert_close(np64(lay.dw2[e].cpu())[:, n_sel], dw2_s[0], MX_TOL, f"{name}:dw2 expert {e}")
+        assert_close(np64(lay.dw13[e].cpu())[cols], dw13_s[0], MX_TOL, f"{name}:dw13 expert {e}")
