@@ -36,7 +36,11 @@ def _compile(src):
 
 
 def build(verbose=True):
+    """Compile every csrc/*.hip and link libmoe.so.  The previous library is
+    removed first, so a failed build leaves no stale library behind."""
     os.makedirs(BUILD, exist_ok=True)
+    if os.path.exists(LIB):
+        os.remove(LIB)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         results = list(ex.map(_compile, srcs))

@@ -17,20 +17,46 @@ constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every range: loa
 
 enum { EPI_STORE = 0, EPI_SWIGLU_FWD = 1, EPI_SWIGLU_BWD = 2 };
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Raw buffer descriptor over [base, base + bytes) as four scalar words
+// (base, base[47:32] with stride 0, num_records, flags).  Loads at or past
+// `bytes` return zero, which masks tile rows / columns / k outside the
+// operand.
+typedef __attribute__((ext_vector_type(4))) uint32_t desc_t;
 
-// Raw buffer resource over [base, base + bytes); loads at or past `bytes`
-// return zero, which masks tile rows / columns / k outside the operand.
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes)
+__device__ __forceinline__ desc_t make_desc(const void* base, int64_t bytes)
 {
-    const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)(bytes < 0 ? 0 : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t n = bytes > 0x7fffffff ? 0x7fffffffu : (uint32_t)(bytes < 0 ? 0 : bytes);
+    return desc_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, n, 0x00020000u};
 }
 
-__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off)
+// a descriptor chosen per wave (the compiler cannot tell it is uniform)
+__device__ __forceinline__ desc_t wave_uniform(desc_t d)
 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
+    return desc_t{(uint32_t)__builtin_amdgcn_readfirstlane(d[0]), (uint32_t)__builtin_amdgcn_readfirstlane(d[1]),
+                  (uint32_t)__builtin_amdgcn_readfirstlane(d[2]), (uint32_t)__builtin_amdgcn_readfirstlane(d[3])};
+}
+
+// Global -> LDS without VGPRs: lane l's BYTES (4 or 16) bytes from
+// desc + voff + soff land at LDS address lds + BYTES * l.  Issued from
+// inline assembly on purpose: the compiler then keeps no record of an
+// asynchronous LDS write and so adds no wait before the LDS reads of the
+// other stage.  The caller owns the ordering: s_waitcnt vmcnt plus a
+// barrier before any wave reads what these loads wrote.  M0 takes the LDS
+// base (M0 is reserved: the compiler sets it wherever it needs it); one wait
+// state separates an M0 write from an LDS DMA.  `desc` and `soff` must be
+// wave-uniform.
+template <int BYTES>
+__device__ __forceinline__ void dma_to_lds(desc_t desc, const void* lds, uint32_t voff, uint32_t soff)
+{
+    const auto lp = (__attribute__((address_space(3))) const void*)lds;
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lp);
+    if constexpr (BYTES == 16)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :: "s"(base), "v"(voff), "s"(desc), "s"(soff) : "memory");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                     :: "s"(base), "v"(voff), "s"(desc), "s"(soff) : "memory");
 }
 
 // A ROWS x BK tile source.  K-major: element (r, k) at p[r*ld + k], rows split
@@ -70,7 +96,7 @@ struct DirectLoader {
     static constexpr int HALF = ROWS / 2;
     static constexpr int CPR_K = BK / 8;                     // 16-byte chunks per K-major row
     static constexpr int RPC_K = 1024 / (BK * 2);            // K-major rows per 1 KB chunk
-    rsrc_t r0, r1;
+    desc_t r0, r1;
     uint32_t off[PER_WAVE];   // per-lane byte offset of its element at k = 0
     uint32_t kstep;           // bytes a K-step advances (scalar)
     int K;
@@ -80,8 +106,8 @@ struct DirectLoader {
         const int w = threadIdx.x >> 6;
         K = s.K;
         if constexpr (!MN) {
-            r0 = make_rsrc(s.p0, (int64_t)s.rows0 * s.ld * 2);
-            r1 = make_rsrc(s.p1, (int64_t)s.rows1 * s.ld * 2);
+            r0 = make_desc(s.p0, (int64_t)s.rows0 * s.ld * 2);
+            r1 = make_desc(s.p1, (int64_t)s.rows1 * s.ld * 2);
             kstep = BK * 2;
 #pragma unroll
             for (int i = 0; i < PER_WAVE; ++i) {
@@ -92,7 +118,7 @@ struct DirectLoader {
                 off[i] = (uint32_t)(rr * s.ld * 2 + c * 16);
             }
         } else {
-            r0 = r1 = make_rsrc(s.p0, (int64_t)s.K * s.ld * 2);
+            r0 = r1 = make_desc(s.p0, (int64_t)s.K * s.ld * 2);
             kstep = (uint32_t)(BK * s.ld * 2);
             constexpr int KROWS = 1024 / (ROWS * 2);   // k-rows per 1 KB chunk
             constexpr int CPR = ROWS / 8;              // 16-byte chunks per k-row
@@ -123,9 +149,7 @@ struct DirectLoader {
             }
             // row block of this instruction: rows [q*RPC_K, ...) lie in the upper half iff q*RPC_K >= HALF
             const bool hi = !MN && i * 4 * RPC_K >= HALF;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(hi ? r1 : r0,
-                                                     (__attribute__((address_space(3))) void*)(tile + q * 512),
-                                                     16, o, so, 0, 0);
+            dma_to_lds<16>(hi ? r1 : r0, tile + q * 512, o, so);
         }
     }
 };

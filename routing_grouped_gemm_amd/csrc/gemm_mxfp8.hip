@@ -49,15 +49,15 @@ struct ScaleLoader {
     static constexpr int PER_WAVE = ROWS / 64 / 4 > 0 ? ROWS / 64 / 4 : 1;
     static constexpr int INSTR = ROWS / 64;   // instructions per tile
     static constexpr int HALF = ROWS / 2;
-    rsrc_t r0, r1;
+    desc_t r0, r1;
     uint32_t off[PER_WAVE];
     __device__ __forceinline__ void init(const MxSrc& s)
     {
         const int lane = threadIdx.x & 63;
         const int w = threadIdx.x >> 6;
         const int64_t lds_ = s.ldc / 32;   // scale row stride in bytes
-        r0 = make_rsrc(s.s0, (int64_t)s.rows0 * lds_);
-        r1 = make_rsrc(s.s1, (int64_t)s.rows1 * lds_);
+        r0 = make_desc(s.s0, (int64_t)s.rows0 * lds_);
+        r1 = make_desc(s.s1, (int64_t)s.rows1 * lds_);
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
             const int q = i * 4 + w;
@@ -74,9 +74,7 @@ struct ScaleLoader {
             const int q = i * 4 + w;
             if (q < INSTR) {
                 const bool hi = q * 64 >= HALF;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(hi ? r1 : r0,
-                                                         (__attribute__((address_space(3))) void*)(tile + q * 256),
-                                                         4, off[i], (uint32_t)kt * 4, 0, 0);
+                dma_to_lds<4>(wave_uniform(hi ? r1 : r0), tile + q * 256, off[i], (uint32_t)kt * 4);
             }
         }
     }
