@@ -204,7 +204,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS void gemm_grouped_m_kernel(MParams p)
 
     f32x16 acc[BM / 64][4];
     mainloop<BM, BK, NS, false, B_MN>(sa, sb, acc, smem);
-    epilogue_m<BM, EPI>(acc, p, row0, rows_valid, nt);
+    epilogue_m<BM, EPI>(acc, p, row0, rows_valid, nt, reinterpret_cast<uint8_t*>(smem));
 }
 
 
@@ -270,8 +270,8 @@ __global__ MOE_GEMM_KERNEL_ATTRS void gemm_grouped_k_kernel(KParams p)
     f32x16 acc[BM / 64][4];
     mainloop<BM, BK, NS, true, true>(sa, sb, acc, smem);
 
-    store_tile<BM>(acc, q.C + (int64_t)e * q.sC + (int64_t)mt * BM * q.ldc, q.ldc, 0, q.M - mt * BM,
-                   nt * BN, q.N);
+    store_tile<BM>(acc, q.C + (int64_t)e * q.sC + (int64_t)mt * BM * q.ldc, q.ldc, q.M - mt * BM, nt * BN,
+                   q.N, reinterpret_cast<uint8_t*>(smem));
 }
 
 template <int BM, int BK, int NS, bool B_MN, int EPI>

@@ -213,70 +213,133 @@ struct MParams {
     int f;                 // SWIGLU: column offset of the u half in gu / dgu
 };
 
+// Epilogues stage the bf16 result tile in LDS (free once the main loop has
+// ended) and store it row by row: each lane writes 16 contiguous bytes and a
+// wave two whole tile rows, instead of 32 rows x 16 bytes per instruction
+// straight from the accumulator layout.  A staged tile is ROWS x (CH*8) bf16,
+// row pitch CH*16 bytes, 16-byte chunk c of row r at chunk c ^ (r & (CH-1)):
+// the 32 rows one accumulator write touches then fall on distinct chunks, and
+// a row read back is one contiguous swizzled row.
+template <int CH>
+__device__ __forceinline__ uint32_t stage_off(int r, int col)   // element (r, col), col % 4 == 0
+{
+    return (uint32_t)(r * (CH * 16) + (((col >> 3) ^ (r & (CH - 1))) << 4) + ((col & 4) << 1));
+}
+
+__device__ __forceinline__ void stage_put(uint8_t* lds, uint32_t off, uint2 v)
+{
+    *reinterpret_cast<uint2*>(lds + off) = v;
+}
+
+// After a barrier: thread t hands out chunks t, t + NTH, ... as put(r, c, v);
+// a trailing barrier frees the LDS again.
+template <int ROWS, int CH, class F>
+__device__ __forceinline__ void stage_flush(const uint8_t* lds, F&& put)
+{
+    __syncthreads();
+#pragma unroll 4
+    for (int q = threadIdx.x; q < ROWS * CH; q += NTH) {
+        const int r = q / CH, c = q % CH;
+        put(r, c, *reinterpret_cast<const uint4*>(lds + r * (CH * 16) + ((c ^ (r & (CH - 1))) << 4)));
+    }
+    __syncthreads();
+}
+
+// the accumulator tile (BM x 256) as bf16 into the staging layout
+template <int BM>
+__device__ __forceinline__ void stage_acc(const f32x16 (&acc)[BM / 64][4], uint8_t* lds)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int i = 0; i < BM / 64; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                stage_put(lds, stage_off<32>(wm * (BM / 2) + i * 32 + (lane & 31), acc_col(wn, j, g, lane)),
+                          pack4_bf16(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                     acc[i][j][4 * g + 3]));
+}
+
 template <int BM, int EPI>
 __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][4], const MParams& p,
-                                           int64_t row0, int rows_valid, int nt)
+                                           int64_t row0, int rows_valid, int nt, uint8_t* lds)
 {
     constexpr int MI = BM / 64;
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    if constexpr (EPI == EPI_STORE) {
+        stage_acc<BM>(acc, lds);
+        stage_flush<BM, 32>(lds, [&](int r, int c, uint4 v) {
+            const int n = nt * BN + 8 * c;
+            if (r < rows_valid && n < p.N) *reinterpret_cast<uint4*>(p.C + (row0 + r) * p.ldc + n) = v;
+        });
+    } else if constexpr (EPI == EPI_SWIGLU_FWD) {
+        // tile columns 0..127 are gate columns n0.., 128..255 the up columns f + n0..
+        const int n0 = nt * 128;
+        stage_acc<BM>(acc, lds);
+        stage_flush<BM, 32>(lds, [&](int r, int c, uint4 v) {
+            const int n = n0 + 8 * (c & 15);
+            if (r < rows_valid && n < p.f)
+                *reinterpret_cast<uint4*>(p.C + (row0 + r) * p.ldc + (c < 16 ? n : p.f + n)) = v;
+        });
+        // h = silu(g) * u from the unrounded fp32 accumulators
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-        const int row = wm * (BM / 2) + i * 32 + (lane & 31);
-        if (row >= rows_valid) continue;
-        const int64_t grow = row0 + row;
-        if constexpr (EPI == EPI_SWIGLU_FWD) {
-            uint16_t* gu_row = p.C + grow * p.ldc;
-            uint16_t* h_row = p.H + grow * p.ldh;
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int n = nt * 128 + acc_col(wn, j, g, lane);
-                    if (n >= p.f) continue;
-                    float gv[4], uv[4];
+                    float hv[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        gv[q] = acc[i][j][4 * g + q];
-                        uv[q] = acc[i][j + 2][4 * g + q];
-                    }
-                    *reinterpret_cast<uint2*>(gu_row + n) = pack4_bf16(gv[0], gv[1], gv[2], gv[3]);
-                    *reinterpret_cast<uint2*>(gu_row + p.f + n) = pack4_bf16(uv[0], uv[1], uv[2], uv[3]);
-                    *reinterpret_cast<uint2*>(h_row + n) =
-                        pack4_bf16(silu_f(gv[0]) * uv[0], silu_f(gv[1]) * uv[1],
-                                   silu_f(gv[2]) * uv[2], silu_f(gv[3]) * uv[3]);
+                    for (int q = 0; q < 4; ++q) hv[q] = silu_f(acc[i][j][4 * g + q]) * acc[i][j + 2][4 * g + q];
+                    stage_put(lds, stage_off<16>(wm * (BM / 2) + i * 32 + (lane & 31), acc_col(wn, j, g, lane)),
+                              pack4_bf16(hv[0], hv[1], hv[2], hv[3]));
                 }
-        } else {
-            uint16_t* c_row = p.C + grow * p.ldc;
+        stage_flush<BM, 16>(lds, [&](int r, int c, uint4 v) {
+            const int n = n0 + 8 * c;
+            if (r < rows_valid && n < p.f) *reinterpret_cast<uint4*>(p.H + (row0 + r) * p.ldh + n) = v;
+        });
+    } else {
+        // SwiGLU backward: dh in the accumulators, g and u from the saved gu;
+        // dg staged and stored first, then du
+        const int n0 = nt * BN;
+#pragma unroll 1
+        for (int half = 0; half < 2; ++half) {
+            // an opaque copy of the base per round: the gu addresses are then
+            // recomputed in each round instead of all kept live across both
+            const uint16_t* G = p.G;
+            asm volatile("" : "+s"(G));
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int i = 0; i < MI; ++i) {
+                const int r = wm * (BM / 2) + i * 32 + (lane & 31);
+                const uint16_t* g_row = G + (row0 + (r < rows_valid ? r : 0)) * p.ldg;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = nt * BN + acc_col(wn, j, g, lane);
-                    if (n >= p.N) continue;
-                    if constexpr (EPI == EPI_STORE) {
-                        *reinterpret_cast<uint2*>(c_row + n) =
-                            pack4_bf16(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                       acc[i][j][4 * g + 3]);
-                    } else {
-                        const uint16_t* g_row = p.G + grow * p.ldg;
-                        float gv[4], uv[4], dg[4], du[4];
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int col = acc_col(wn, j, g, lane);
+                        const int n = n0 + col < p.N ? n0 + col : 0;
+                        float gv[4], uv[4], o[4];
                         unpack4_bf16(*reinterpret_cast<const uint2*>(g_row + n), gv);
                         unpack4_bf16(*reinterpret_cast<const uint2*>(g_row + p.f + n), uv);
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const float dh = acc[i][j][4 * g + q];
                             const float sg = 1.0f / (1.0f + __expf(-gv[q]));
-                            du[q] = dh * gv[q] * sg;
-                            dg[q] = dh * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
+                            o[q] = half ? dh * gv[q] * sg : dh * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
                         }
-                        *reinterpret_cast<uint2*>(c_row + n) = pack4_bf16(dg[0], dg[1], dg[2], dg[3]);
-                        *reinterpret_cast<uint2*>(c_row + p.f + n) = pack4_bf16(du[0], du[1], du[2], du[3]);
+                        stage_put(lds, stage_off<32>(r, col), pack4_bf16(o[0], o[1], o[2], o[3]));
                     }
-                }
+                // one row block's gu loads live at a time (hoisting all of them spills)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            stage_flush<BM, 32>(lds, [&](int r, int c, uint4 v) {
+                const int n = n0 + 8 * c;
+                if (r < rows_valid && n < p.N)
+                    *reinterpret_cast<uint4*>(p.C + (row0 + r) * p.ldc + (half ? p.f + n : n)) = v;
+            });
         }
     }
 }
@@ -320,33 +383,17 @@ __device__ __forceinline__ bool schedule_m(const int32_t* group_off, int capacit
     return true;
 }
 
-// store a BM x 256 accumulator tile (transposed layout above) as bf16 rows of C
+// store a BM x 256 accumulator tile as bf16 rows of C (rows [0, rows), columns
+// col0 + [0, 256) below N), through the LDS staging above
 template <int BM>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[BM / 64][4], uint16_t* C, int64_t ldc,
-                                           int row_lo, int rows, int col0, int N)
+                                           int rows, int col0, int N, uint8_t* lds)
 {
-    constexpr int MI = BM / 64;
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-        const int m = wm * (BM / 2) + i * 32 + (lane & 31);
-        if (m >= rows) continue;
-        uint16_t* c_row = C + (int64_t)(row_lo + m) * ldc;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = col0 + acc_col(wn, j, g, lane);
-                if (n < N)
-                    *reinterpret_cast<uint2*>(c_row + n) =
-                        pack4_bf16(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                   acc[i][j][4 * g + 3]);
-            }
-    }
+    stage_acc<BM>(acc, lds);
+    stage_flush<BM, 32>(lds, [&](int r, int c, uint4 v) {
+        const int n = col0 + 8 * c;
+        if (r < rows && n < N) *reinterpret_cast<uint4*>(C + r * ldc + n) = v;
+    });
 }
 
 }  // namespace gemm

@@ -241,7 +241,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS void mx_grouped_m_kernel(MxMParams mp)
 
     f32x16 acc[BM / 64][4];
     mainloop_mx<BM>(sa, sb, acc, smem);
-    epilogue_m<BM, EPI>(acc, p, tile.row0, tile.rows_valid, nt);
+    epilogue_m<BM, EPI>(acc, p, tile.row0, tile.rows_valid, nt, smem);
 }
 
 // weight gradient over group-transposed operands: C_e = A_e B_e^T with
@@ -315,7 +315,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS void mx_grouped_k_kernel(MxKParams p)
 
     f32x16 acc[BM / 64][4];
     mainloop_mx<BM>(sa, sb, acc, smem);
-    store_tile<BM>(acc, q.C + (int64_t)e * q.sC + a_row0 * q.ldc, q.ldc, 0, arows, nt * BN, q.N);
+    store_tile<BM>(acc, q.C + (int64_t)e * q.sC + a_row0 * q.ldc, q.ldc, arows, nt * BN, q.N, smem);
 }
 
 constexpr int kMxBM = 256;
