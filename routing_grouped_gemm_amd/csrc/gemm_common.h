@@ -154,7 +154,10 @@ struct DirectLoader {
     }
 };
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+// logistic function with the hardware reciprocal (about 1 ulp; results are
+// stored as bf16), and silu(g) = g * sigmoid(g)
+__device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu_f(float g) { return g * sigmoid_f(g); }
 
 // first column (0..255) of the 32-wide sub-tile j of wave column wn
 __device__ __forceinline__ int sub_col(int wn, int j) { return (j >> 1) * 128 + wn * 64 + (j & 1) * 32; }
@@ -267,7 +270,8 @@ __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][4], cons
                                            int64_t row0, int rows_valid, int nt, uint8_t* lds)
 {
     constexpr int MI = BM / 64;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int lane = threadIdx.x & 63;
     const int wm = wave >> 1, wn = wave & 1;
     if constexpr (EPI == EPI_STORE) {
         stage_acc<BM>(acc, lds);
@@ -302,44 +306,63 @@ __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][4], cons
             if (r < rows_valid && n < p.f) *reinterpret_cast<uint4*>(p.H + (row0 + r) * p.ldh + n) = v;
         });
     } else {
-        // SwiGLU backward: dh in the accumulators, g and u from the saved gu;
-        // dg staged and stored first, then du
+        // SwiGLU backward, 128 tile columns at a time (accumulator sub-tiles
+        // j = 2*ch, 2*ch+1 of every wave): the g and u tiles of those columns
+        // come into LDS (direct loads, staging layout), every lane overwrites
+        // its g, u pairs in place with dg, du, and both tiles leave as rows of dgu
+        constexpr int QTILE = BM * 16 * 16;                 // bytes of one BM x 128 bf16 tile
+        static_assert(2 * QTILE <= 2 * (BM + BN) * 64 * 2, "staging fits the stage buffers");
         const int n0 = nt * BN;
-#pragma unroll 1
-        for (int half = 0; half < 2; ++half) {
-            // an opaque copy of the base per round: the gu addresses are then
-            // recomputed in each round instead of all kept live across both
-            const uint16_t* G = p.G;
-            asm volatile("" : "+s"(G));
+        uint8_t* lg = lds;
+        uint8_t* lu = lds + QTILE;
+        const desc_t g_desc = make_desc(p.G + row0 * p.ldg, (int64_t)rows_valid * p.ldg * 2);
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const int r = wm * (BM / 2) + i * 32 + (lane & 31);
-                const uint16_t* g_row = G + (row0 + (r < rows_valid ? r : 0)) * p.ldg;
+        for (int ch = 0; ch < 2; ++ch) {
+            const int nc = n0 + 128 * ch;                   // first column of this half
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+            for (int i = 0; i < QTILE / 1024 / 4; ++i) {
+                const int q = i * 4 + wave;                 // 1 KB slice of the tile
+                const int slot = q * 64 + lane;             // 16-byte staging slot
+                const int r = slot >> 4, c = (slot & 15) ^ (r & 15);
+                const uint32_t off = (uint32_t)((r * p.ldg + nc + 8 * c) * 2);
+                dma_to_lds<16>(g_desc, lg + q * 1024, off, 0);
+                dma_to_lds<16>(g_desc, lu + q * 1024, off, (uint32_t)(p.f * 2));
+            }
+            wait_vmcnt<0>();
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        const int col = acc_col(wn, j, g, lane);
-                        const int n = n0 + col < p.N ? n0 + col : 0;
-                        float gv[4], uv[4], o[4];
-                        unpack4_bf16(*reinterpret_cast<const uint2*>(g_row + n), gv);
-                        unpack4_bf16(*reinterpret_cast<const uint2*>(g_row + p.f + n), uv);
+                        const int j = 2 * ch + jj;
+                        const uint32_t off = stage_off<16>(wm * (BM / 2) + i * 32 + (lane & 31),
+                                                           acc_col(wn, j, g, lane) - 128 * ch);
+                        float gv[4], uv[4], dgv[4], duv[4];
+                        unpack4_bf16(*reinterpret_cast<const uint2*>(lg + off), gv);
+                        unpack4_bf16(*reinterpret_cast<const uint2*>(lu + off), uv);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float dh = acc[i][j][4 * g + q];
-                            const float sg = 1.0f / (1.0f + __expf(-gv[q]));
-                            o[q] = half ? dh * gv[q] * sg : dh * uv[q] * sg * (1.0f + gv[q] * (1.0f - sg));
+                        for (int t = 0; t < 4; ++t) {
+                            const float dh = acc[i][j][4 * g + t];
+                            const float sg = sigmoid_f(gv[t]);
+                            duv[t] = dh * gv[t] * sg;
+                            dgv[t] = dh * uv[t] * sg * (1.0f + gv[t] * (1.0f - sg));
                         }
-                        stage_put(lds, stage_off<32>(r, col), pack4_bf16(o[0], o[1], o[2], o[3]));
+                        stage_put(lg, off, pack4_bf16(dgv[0], dgv[1], dgv[2], dgv[3]));
+                        stage_put(lu, off, pack4_bf16(duv[0], duv[1], duv[2], duv[3]));
                     }
-                // one row block's gu loads live at a time (hoisting all of them spills)
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            stage_flush<BM, 32>(lds, [&](int r, int c, uint4 v) {
-                const int n = n0 + 8 * c;
+            __syncthreads();
+#pragma unroll 4
+            for (int q = threadIdx.x; q < BM * 16 * 2; q += NTH) {
+                const int which = q / (BM * 16), qq = q % (BM * 16);
+                const int r = qq >> 4, c = qq & 15;
+                const int n = nc + 8 * c;
+                const uint4 v = *reinterpret_cast<const uint4*>((which ? lu : lg) + r * 256 + ((c ^ (r & 15)) << 4));
                 if (r < rows_valid && n < p.N)
-                    *reinterpret_cast<uint4*>(p.C + (row0 + r) * p.ldc + (half ? p.f + n : n)) = v;
-            });
+                    *reinterpret_cast<uint4*>(p.C + (row0 + r) * p.ldc + (which ? p.f + n : n)) = v;
+            }
+            __syncthreads();
         }
     }
 }
