@@ -11,10 +11,14 @@
 // MXFP8 (tutorial, MXFP8 section): one E8M0 scale per 32 elements, the
 // smallest power of two that keeps the block maximum within 448, codes by
 // round-to-nearest-even into E4M3FN.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t vu4;   // 16 bytes, for non-temporal access
 
 // 8 x bf16 or 4 x fp32 per 16-byte vector
 template <bool BF16>
@@ -37,10 +41,12 @@ __device__ __forceinline__ uint4 scale_vec(uint4 v, float s)
     }
 }
 
-// thread i handles vector (i % nvec) of token row (i / nvec)
-template <bool BF16, bool SCALE>
+// thread i handles vector (i % nvec) of token row (i / nvec).  K (= top-k)
+// is a template parameter: the token's K destinations and scales are read
+// first, then its K stores go out back to back.
+template <bool BF16, bool SCALE, int K>
 __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x, int T, int nvec,
-                                                      int k, const int32_t* __restrict__ dst_row,
+                                                      const int32_t* __restrict__ dst_row,
                                                       const float* __restrict__ row_scale,
                                                       int64_t n_rows, uint4* __restrict__ x_perm,
                                                       int32_t* __restrict__ dev_err)
@@ -49,18 +55,21 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ 
     if (i >= (int64_t)T * nvec) return;
     const int64_t t = i / nvec;
     const int v = (int)(i - t * nvec);
+    int32_t dst[K];
+    float sc[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) dst[j] = dst_row[t * K + j];
+    if constexpr (SCALE) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) sc[j] = row_scale[t * K + j];
+    }
     const uint4 val = x[i];
     bool bad = false;
-    for (int j = 0; j < k; ++j) {
-        const int64_t dst = dst_row[t * k + j];
-        if (dst < 0) continue;
-        if (dst >= n_rows) {
-            bad = true;
-            continue;
-        }
-        uint4 o = val;
-        if constexpr (SCALE) o = scale_vec<BF16>(val, row_scale[t * k + j]);
-        x_perm[dst * nvec + v] = o;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        bad |= dst[j] >= n_rows;
+        if (dst[j] < 0 || dst[j] >= n_rows) continue;
+        x_perm[(int64_t)dst[j] * nvec + v] = SCALE ? scale_vec<BF16>(val, sc[j]) : val;
     }
     if (bad && dev_err) atomicOr(dev_err, (int)MOE_ERR_ROW_RANGE);
 }
@@ -237,12 +246,14 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
     scales[(int64_t)K * P / 32 + (int64_t)c * (mpad / 32) + rb] = (uint8_t)(e + 127);
 }
 
-template <bool BF16>
+// thread i makes vector (i % nvec) of token (i / nvec): the K destination
+// rows and weights are read first, then the K row loads are all in flight
+// before the fp32 accumulation in slot order.
+template <bool BF16, int K>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y,
                                                       const int32_t* __restrict__ dst_row,
-                                                      const float* __restrict__ w, int T, int k,
-                                                      int nvec, int64_t n_rows,
-                                                      uint4* __restrict__ out,
+                                                      const float* __restrict__ w, int T, int nvec,
+                                                      int64_t n_rows, uint4* __restrict__ out,
                                                       int32_t* __restrict__ dev_err)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -250,41 +261,69 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     const int64_t t = i / nvec;
     const int v = (int)(i - t * nvec);
     constexpr int NE = BF16 ? 8 : 4;
+    int32_t dst[K];
+    float wt[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) dst[j] = dst_row[t * K + j];
+#pragma unroll
+    for (int j = 0; j < K; ++j) wt[j] = w ? w[t * K + j] : 1.0f;
+    // the expert rows are read once and the output written once: both
+    // streams are non-temporal (they do not displace what the GEMMs reuse)
+    vu4 val[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        val[j] = vu4{0, 0, 0, 0};
+        if (dst[j] >= 0 && dst[j] < n_rows)
+            val[j] = __builtin_nontemporal_load(reinterpret_cast<const vu4*>(y) + (int64_t)dst[j] * nvec + v);
+    }
     float acc[NE];
 #pragma unroll
     for (int q = 0; q < NE; ++q) acc[q] = 0.0f;
     bool bad = false;
-    for (int j = 0; j < k; ++j) {
-        const int64_t dst = dst_row[t * k + j];
-        if (dst < 0) continue;
-        if (dst >= n_rows) {
-            bad = true;
-            continue;
-        }
-        const float wt = w ? w[t * k + j] : 1.0f;
-        const uint4 val = y[dst * nvec + v];
-        const uint32_t ww[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        bad |= dst[j] >= n_rows;
+        if (dst[j] < 0 || dst[j] >= n_rows) continue;
+        const uint32_t ww[4] = {val[j][0], val[j][1], val[j][2], val[j][3]};
         if constexpr (BF16) {
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                acc[2 * p] = fmaf(wt, bf16_lo(ww[p]), acc[2 * p]);
-                acc[2 * p + 1] = fmaf(wt, bf16_hi(ww[p]), acc[2 * p + 1]);
+                acc[2 * p] = fmaf(wt[j], bf16_lo(ww[p]), acc[2 * p]);
+                acc[2 * p + 1] = fmaf(wt[j], bf16_hi(ww[p]), acc[2 * p + 1]);
             }
         } else {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) acc[p] = fmaf(wt, __uint_as_float(ww[p]), acc[p]);
+            for (int p = 0; p < 4; ++p) acc[p] = fmaf(wt[j], __uint_as_float(ww[p]), acc[p]);
         }
     }
-    uint4 o;
+    vu4 o;
     if constexpr (BF16) {
-        o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                       pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+        o = vu4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                pack_bf16x2(acc[6], acc[7])};
     } else {
-        o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
-                       __float_as_uint(acc[3]));
+        o = vu4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                __float_as_uint(acc[3])};
     }
-    out[i] = o;
+    __builtin_nontemporal_store(o, reinterpret_cast<vu4*>(out) + i);
     if (bad && dev_err) atomicOr(dev_err, (int)MOE_ERR_ROW_RANGE);
+}
+
+// run f(integral_constant<int, k>) for k in 1..kMaxTopK
+template <class F>
+hipError_t with_k(int k, F&& f)
+{
+    switch (k) {
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 3: f(std::integral_constant<int, 3>{}); break;
+    case 4: f(std::integral_constant<int, 4>{}); break;
+    case 5: f(std::integral_constant<int, 5>{}); break;
+    case 6: f(std::integral_constant<int, 6>{}); break;
+    case 7: f(std::integral_constant<int, 7>{}); break;
+    case 8: f(std::integral_constant<int, 8>{}); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipSuccess;
 }
 
 inline unsigned grid_for(int64_t n) { return (unsigned)((n + 255) / 256); }
@@ -313,18 +352,22 @@ hipError_t launch_permute(int dtype, const void* x, int T, int d, int k, const i
     const int64_t n = (int64_t)T * nvec;
     if (n > 0) {
         const dim3 grid(grid_for(n)), blk(256);
-        if (bf && row_scale)
-            hipLaunchKernelGGL((permute_kernel<true, true>), grid, blk, 0, s, (const uint4*)x, T,
-                               nvec, k, dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
-        else if (bf)
-            hipLaunchKernelGGL((permute_kernel<true, false>), grid, blk, 0, s, (const uint4*)x, T,
-                               nvec, k, dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
-        else if (row_scale)
-            hipLaunchKernelGGL((permute_kernel<false, true>), grid, blk, 0, s, (const uint4*)x, T,
-                               nvec, k, dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
-        else
-            hipLaunchKernelGGL((permute_kernel<false, false>), grid, blk, 0, s, (const uint4*)x, T,
-                               nvec, k, dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
+        const hipError_t e = with_k(k, [&](auto kc) {
+            constexpr int K = decltype(kc)::value;
+            if (bf && row_scale)
+                hipLaunchKernelGGL((permute_kernel<true, true, K>), grid, blk, 0, s, (const uint4*)x, T, nvec,
+                                   dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
+            else if (bf)
+                hipLaunchKernelGGL((permute_kernel<true, false, K>), grid, blk, 0, s, (const uint4*)x, T, nvec,
+                                   dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
+            else if (row_scale)
+                hipLaunchKernelGGL((permute_kernel<false, true, K>), grid, blk, 0, s, (const uint4*)x, T, nvec,
+                                   dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
+            else
+                hipLaunchKernelGGL((permute_kernel<false, false, K>), grid, blk, 0, s, (const uint4*)x, T, nvec,
+                                   dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
+        });
+        if (e != hipSuccess) return e;
     }
     if (padded && n_rows > 0)
         hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)((n_rows + 15) / 16)), dim3(256), 0, s,
@@ -340,14 +383,16 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* dst_row,
     const int nvec = bf ? d / 8 : d / 4;
     const int64_t n = (int64_t)T * nvec;
     if (n > 0) {
-        if (bf)
-            hipLaunchKernelGGL((combine_kernel<true>), dim3(grid_for(n)), dim3(256), 0, s,
-                               (const uint4*)y_perm, dst_row, w, T, k, nvec, n_rows, (uint4*)out,
-                               dev_err);
-        else
-            hipLaunchKernelGGL((combine_kernel<false>), dim3(grid_for(n)), dim3(256), 0, s,
-                               (const uint4*)y_perm, dst_row, w, T, k, nvec, n_rows, (uint4*)out,
-                               dev_err);
+        const hipError_t e = with_k(k, [&](auto kc) {
+            constexpr int K = decltype(kc)::value;
+            if (bf)
+                hipLaunchKernelGGL((combine_kernel<true, K>), dim3(grid_for(n)), dim3(256), 0, s,
+                                   (const uint4*)y_perm, dst_row, w, T, nvec, n_rows, (uint4*)out, dev_err);
+            else
+                hipLaunchKernelGGL((combine_kernel<false, K>), dim3(grid_for(n)), dim3(256), 0, s,
+                                   (const uint4*)y_perm, dst_row, w, T, nvec, n_rows, (uint4*)out, dev_err);
+        });
+        if (e != hipSuccess) return e;
     }
     return hipGetLastError();
 }

@@ -5,14 +5,15 @@
 // and the per-expert permutation are produced on the GPU so the loop never
 // waits for the host.  Three kernels, all deterministic (no atomics decide
 // an order):
-//   1. route_topk_kernel: one segment of LPT lanes per token selects the k
-//      largest fp32 logits by k rounds of a segmented butterfly arg-max
-//      (ties -> lower expert index), computes the softmax over the selected
-//      logits, and for its block of 64 tokens the per-expert histogram and
-//      each pair's rank among the block's earlier pairs of the same expert.
-//   2. route_scan_kernel (one workgroup): column prefix sums of the block
-//      histograms (-> each block's base rank per expert), counts, and the
-//      exclusive scan of counts (-> offsets).
+//   1. route_topk_kernel: one segment of LPT lanes per token (16 logits per
+//      lane) selects the k largest fp32 logits by k rounds of a lane-local
+//      pass and a segmented butterfly arg-max (ties -> lower expert index),
+//      computes the softmax over the selected logits, and for its block of
+//      64 tokens the per-expert histogram (stored expert-major) and each
+//      pair's rank among the block's earlier pairs of the same expert.
+//   2. route_scan_kernel (one workgroup): prefix sums along each expert's
+//      row of block histograms (-> each block's base rank per expert),
+//      counts, and the exclusive scan of counts (-> offsets).
 //   3. route_finalize_kernel: dst_row = offsets[e] + base + local rank (or
 //      the padded row), src_slot as its inverse, padding rows -1.
 #include "moe_internal.h"
@@ -32,17 +33,21 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2)
     return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
-// LPT lanes per token (power of two, <= 64); VPL logits per lane (E <= LPT*VPL)
-template <int LPT, int VPL>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
-                                                         int E, int k,
+// LPT lanes per token (power of two, <= 64); lane l of a token's segment owns
+// the VPL consecutive logits [l*VPL, l*VPL + VPL) (E <= LPT*VPL).  A block of
+// NTHR = min(TB * LPT, 1024) threads handles TB tokens, NTHR/LPT at a time
+// (all of them at once up to 16 lanes per token).
+template <int LPT, int VPL, int NTHR = (TB * LPT < 1024 ? (TB * LPT < 64 ? 64 : TB * LPT) : 1024)>
+__global__ __launch_bounds__(NTHR) void route_topk_kernel(const float* __restrict__ logits, int T,
+                                                         int E, int k, int nblk,
                                                          int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_w,
                                                          int32_t* __restrict__ lrank,
                                                          int32_t* __restrict__ hist,
                                                          int32_t* __restrict__ dev_err)
 {
-    constexpr int TPI = 256 / LPT;  // tokens handled concurrently by the block
+    constexpr int TPI = NTHR / LPT;  // tokens handled concurrently by the block
+    static_assert(VPL <= 32, "taken mask");
     __shared__ int s_exp[TB * kMaxTopK];
     __shared__ int s_hist[kMaxExperts];
 
@@ -51,26 +56,36 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     const int seg = tid / LPT;
     const int t0 = blockIdx.x * TB;
     const int nt = min(TB, T - t0);
+    // 16-byte loads of whole lane ranges when every row start is 16-byte aligned
+    const bool vec = (E % 4) == 0 && (VPL % 4) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
 
-    for (int e = tid; e < E; e += 256) s_hist[e] = 0;
+    for (int e = tid; e < E; e += NTHR) s_hist[e] = 0;
 
     bool bad = false;
     for (int tl = seg; tl < TB; tl += TPI) {
         const int t = t0 + tl;
         const bool active = tl < nt;
+        const int e0 = lane * VPL;
         float v[VPL];
+        if (vec && active && e0 + VPL <= E) {
+            const float4* src = reinterpret_cast<const float4*>(logits + (int64_t)t * E + e0);
+#pragma unroll
+            for (int s = 0; s < VPL / 4; ++s) {
+                const float4 q = src[s];
+                v[4 * s] = q.x;
+                v[4 * s + 1] = q.y;
+                v[4 * s + 2] = q.z;
+                v[4 * s + 3] = q.w;
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < VPL; ++s)
+                v[s] = active && e0 + s < E ? logits[(int64_t)t * E + e0 + s] : -INFINITY;
+        }
 #pragma unroll
         for (int s = 0; s < VPL; ++s) {
-            const int e = lane + s * LPT;
-            float x = -INFINITY;
-            if (active && e < E) {
-                x = logits[(int64_t)t * E + e];
-                if (!__builtin_isfinite(x)) {
-                    bad = true;
-                    x = -INFINITY;
-                }
-            }
-            v[s] = x;
+            if (active && e0 + s < E && !__builtin_isfinite(v[s])) bad = true;
+            if (!__builtin_isfinite(v[s])) v[s] = -INFINITY;
         }
         uint32_t taken = 0;
         float sel_v[kMaxTopK];
@@ -83,7 +98,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
                 int bi = 0x7fffffff;
 #pragma unroll
                 for (int s = 0; s < VPL; ++s) {
-                    const int e = lane + s * LPT;
+                    const int e = e0 + s;
                     if (e < E && !(taken & (1u << s)) && better(v[s], e, bv, bi)) {
                         bv = v[s];
                         bi = e;
@@ -99,7 +114,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
                         bi = oi;
                     }
                 }
-                if (bi % LPT == lane) taken |= 1u << (bi / LPT);
+                if (bi / VPL == lane) taken |= 1u << (bi % VPL);
                 sel_v[j] = bv;
                 sel_i[j] = bi;
             }
@@ -132,7 +147,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 
     // rank of each pair among the block's earlier pairs of the same expert
     const int P = nt * k;
-    for (int p = tid; p < P; p += 256) {
+    for (int p = tid; p < P; p += NTHR) {
         const int e = s_exp[p];
         int r = 0;
         for (int q = 0; q < p; ++q) r += (s_exp[q] == e);
@@ -140,57 +155,63 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
         atomicAdd(&s_hist[e], 1);  // integer count: order-independent
     }
     __syncthreads();
-    for (int e = tid; e < E; e += 256) hist[(int64_t)blockIdx.x * E + e] = s_hist[e];
+    // expert-major: hist[e][block]
+    for (int e = tid; e < E; e += NTHR) hist[(int64_t)e * nblk + blockIdx.x] = s_hist[e];
 }
 
-// One workgroup of 1024 threads.  hist [nblk, E] is replaced by its exclusive
-// column prefix (the first rank of each block per expert).
-__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ hist, int nblk,
-                                                          int E, int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ offsets)
+// One wave per expert: hist [E, nblk] (expert-major) is replaced by its
+// exclusive prefix along each expert's row (the first rank of each block
+// per expert) and counts[e] is the row total.  Each lane takes 8 consecutive
+// blocks per chunk of 512, all loads of a chunk in flight together.
+__global__ __launch_bounds__(256) void route_scan_kernel(int32_t* __restrict__ hist, int nblk,
+                                                         int E, int32_t* __restrict__ counts)
 {
-    __shared__ int s_part[1024];
-    __shared__ int s_cnt[kMaxExperts];
-    __shared__ int s_wsum[16];
-    const int tid = threadIdx.x;
-
-    const int ech = E < 1024 ? E : 1024;          // experts per pass
-    const int S = 1024 / ech;                     // row segments per expert
-    for (int e0 = 0; e0 < E; e0 += ech) {
-        const int el = tid % ech;
-        const int s = tid / ech;
-        const int e = e0 + el;
-        const bool act = s < S && e < E;
-        const int r0 = (int)((int64_t)nblk * s / S);
-        const int r1 = (int)((int64_t)nblk * (s + 1) / S);
-        int part = 0;
-        if (act)
-            for (int r = r0; r < r1; ++r) part += hist[(int64_t)r * E + e];
-        s_part[tid] = part;
-        __syncthreads();
-        if (act) {
-            int base = 0, total = 0;
-            for (int q = 0; q < S; ++q) {
-                const int pv = s_part[q * ech + el];
-                if (q < s) base += pv;
-                total += pv;
-            }
-            for (int r = r0; r < r1; ++r) {
-                const int c = hist[(int64_t)r * E + e];
-                hist[(int64_t)r * E + e] = base;
-                base += c;
-            }
-            if (s == 0) {
-                counts[e] = total;
-                s_cnt[e] = total;
-            }
+    constexpr int CH = 8;
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= E) return;
+    int32_t* row = hist + (int64_t)e * nblk;
+    int carry = 0;
+    for (int c0 = 0; c0 < nblk; c0 += 64 * CH) {
+        const int b0 = c0 + lane * CH;
+        int v[CH];
+#pragma unroll
+        for (int q = 0; q < CH; ++q) v[q] = b0 + q < nblk ? row[b0 + q] : 0;
+        int sum = 0;
+#pragma unroll
+        for (int q = 0; q < CH; ++q) sum += v[q];
+        // wave inclusive scan of the lane sums
+        int incl = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += o;
         }
-        __syncthreads();
+        int run = carry + incl - sum;
+#pragma unroll
+        for (int q = 0; q < CH; ++q) {
+            if (b0 + q < nblk) row[b0 + q] = run;
+            run += v[q];
+        }
+        carry += __shfl(incl, 63, 64);
     }
-    // exclusive scan of counts -> offsets (E <= 1024, one value per thread)
-    const int wave = tid / 64, lane = tid % 64;
-    int v = tid < E ? s_cnt[tid] : 0;
-    int incl = v;
+    if (lane == 0) counts[e] = carry;
+}
+
+// exclusive scan of counts[0..E) into s_off[0..E] by one block of 256 threads
+__device__ __forceinline__ void block_offsets(const int32_t* __restrict__ counts, int E, int* s_off,
+                                              int* s_wsum)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int PER = kMaxExperts / 256;   // 4 counts per thread
+    int v[PER], sum = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int e = tid * PER + q;
+        v[q] = e < E ? counts[e] : 0;
+        sum += v[q];
+    }
+    int incl = sum;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const int o = __shfl_up(incl, off, 64);
@@ -198,29 +219,41 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* __restrict__ 
     }
     if (lane == 63) s_wsum[wave] = incl;
     __syncthreads();
-    int wbase = 0;
-    for (int w = 0; w < wave; ++w) wbase += s_wsum[w];
-    if (tid < E) offsets[tid] = wbase + incl - v;
-    if (tid == E - 1) offsets[E] = wbase + incl;
-    if (E == 0 && tid == 0) offsets[0] = 0;
+    int run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += s_wsum[w];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int e = tid * PER + q;
+        if (e < E) s_off[e] = run;
+        run += v[q];
+    }
+    if (tid == 255) s_off[E] = run;   // the last thread ends on the grand total
+    __syncthreads();
 }
 
+// dst_row / src_slot of every pair; each block first forms the expert
+// offsets (exclusive scan of counts) in LDS, block 0 also stores them
 __global__ __launch_bounds__(256) void route_finalize_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ lrank,
-    const int32_t* __restrict__ base, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ counts, int T, int E, int k, int C, int32_t* __restrict__ dst_row,
-    int32_t* __restrict__ src_slot, int64_t total)
+    const int32_t* __restrict__ base, int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ counts, int T, int E, int k, int C, int nblk,
+    int32_t* __restrict__ dst_row, int32_t* __restrict__ src_slot, int64_t total)
 {
+    __shared__ int s_off[kMaxExperts + 1];
+    __shared__ int s_wsum[4];
+    block_offsets(counts, E, s_off, s_wsum);
+    if (blockIdx.x == 0)
+        for (int e = threadIdx.x; e <= E; e += 256) offsets[e] = s_off[e];
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= total) return;
     const int64_t P = (int64_t)T * k;
     if (i < P) {
         const int64_t t = i / k;
         const int e = topk_idx[i];
-        const int rank = base[(t / TB) * E + e] + lrank[i];
+        const int rank = base[(int64_t)e * nblk + t / TB] + lrank[i];
         int64_t dst;
         if (C > 0) dst = rank < C ? (int64_t)e * C + rank : -1;
-        else dst = (int64_t)offsets[e] + rank;
+        else dst = (int64_t)s_off[e] + rank;
         dst_row[i] = (int32_t)dst;
         if (dst >= 0) src_slot[dst] = (int32_t)i;
     }
@@ -236,8 +269,9 @@ void launch_topk(int nblk, hipStream_t s, const float* logits, int T, int E, int
                  int32_t* topk_idx, float* topk_w, int32_t* lrank, int32_t* hist,
                  int32_t* dev_err)
 {
-    hipLaunchKernelGGL((route_topk_kernel<LPT, VPL>), dim3(nblk), dim3(256), 0, s, logits, T, E,
-                       k, topk_idx, topk_w, lrank, hist, dev_err);
+    constexpr int NTHR = TB * LPT < 1024 ? (TB * LPT < 64 ? 64 : TB * LPT) : 1024;
+    hipLaunchKernelGGL((route_topk_kernel<LPT, VPL, NTHR>), dim3(nblk), dim3(NTHR), 0, s, logits, T, E,
+                       k, nblk, topk_idx, topk_w, lrank, hist, dev_err);
 }
 
 }  // namespace
@@ -249,22 +283,25 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int capacity, 
 {
     const int nblk = (T + TB - 1) / TB;
     if (nblk > 0) {
-        if (E <= 8) launch_topk<8, 1>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
-        else if (E <= 16) launch_topk<16, 1>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
-        else if (E <= 32) launch_topk<32, 1>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
-        else if (E <= 64) launch_topk<64, 1>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
-        else if (E <= 128) launch_topk<64, 2>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
-        else if (E <= 256) launch_topk<64, 4>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
-        else if (E <= 512) launch_topk<64, 8>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
+        // 16 logits per lane (8 below 9 experts): a token's segment is E/16 lanes
+        if (E <= 8) launch_topk<1, 8>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
+        else if (E <= 16) launch_topk<1, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
+        else if (E <= 32) launch_topk<2, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
+        else if (E <= 64) launch_topk<4, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
+        else if (E <= 128) launch_topk<8, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
+        else if (E <= 256) launch_topk<16, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
+        else if (E <= 512) launch_topk<32, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
         else launch_topk<64, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
     }
-    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, hist, nblk, E, counts, offsets);
+    // also for T = 0: the scan then writes zero counts
+    hipLaunchKernelGGL(route_scan_kernel, dim3((unsigned)((E + 3) / 4)), dim3(256), 0, s, hist, nblk, E,
+                       counts);
     const int64_t P = (int64_t)T * k;
     const int64_t total = capacity > 0 ? (P > n_rows ? P : n_rows) : P;
-    if (total > 0) {
-        const int64_t grid = (total + 255) / 256;
+    {   // at least one block: it stores the offsets
+        const int64_t grid = total > 0 ? (total + 255) / 256 : 1;
         hipLaunchKernelGGL(route_finalize_kernel, dim3((unsigned)grid), dim3(256), 0, s, topk_idx,
-                           lrank, hist, offsets, counts, T, E, k, capacity, dst_row, src_slot,
+                           lrank, hist, offsets, counts, T, E, k, capacity, nblk, dst_row, src_slot,
                            total);
     }
     return hipGetLastError();
