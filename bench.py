@@ -38,8 +38,11 @@ KERNEL_NAMES = {
     "gemm_dgrad_down": "gemm_grouped_m_kernel<256, 64, 2, true, 2> (dgrad down + SwiGLU bwd)",
     "gemm_dgrad_gate_up": "gemm_grouped_m_kernel<256, 64, 2, true, 0> (dgrad gate/up)",
     "gemm_wgrad": "gemm_grouped_k_kernel<256, 64, 2> (wgrad, dWd and dW13 in one launch)",
-    "permute": "permute_kernel<true, false>",
-    "combine": "combine_kernel<true>",
+    "permute": "permute_kernel<true, false, {k}>",
+    "combine": "combine_kernel<true, {k}>",
+    "combine_bwd": "permute_kernel<true, true, {k}>",
+    "permute_bwd": "combine_kernel<true, {k}>",
+    "route": "route_topk_kernel + route_scan_kernel + route_finalize_kernel",
 }
 KERNEL_NAMES_MX = {
     "gemm_gate_up": "mx_grouped_m_kernel<256, 1> (gate/up + SwiGLU)",
@@ -48,8 +51,16 @@ KERNEL_NAMES_MX = {
     "gemm_dgrad_gate_up": "quant_rows_kernel (dgu) + mx_grouped_m_kernel<256, 0> (dgrad gate/up)",
     "gemm_wgrad": "4 x quant_cols_kernel + mx_grouped_k_kernel<256> (wgrad, dWd and dW13)",
     "permute": "permute_mx_kernel",
-    "combine": "combine_kernel<true>",
+    "combine": "combine_kernel<true, {k}>",
+    "combine_bwd": "permute_kernel<true, true, {k}>",
+    "permute_bwd": "combine_kernel<true, {k}>",
+    "route": "route_topk_kernel + route_scan_kernel + route_finalize_kernel",
 }
+
+
+def kernel_name(stage, k, mx=False):
+    """The kernel(s) a stage launches (templates as the profiler names them)."""
+    return (KERNEL_NAMES_MX if mx else KERNEL_NAMES).get(stage, stage).format(k=k)
 
 
 PROFILES = os.path.join(ROOT, "profiles")
@@ -346,7 +357,7 @@ def main():
               "unit": "GB/s", "frac": round(by / dom_ms / 1e6 / PEAK_HBM_GBS, 4)}
     rl["attainable"] = round(roofline(peak, PEAK_HBM_GBS / 1e3, fl / by), 1) if fl else None
     rl.update({"traffic": measured_traffic(dom, args.workload + ("_padded" if args.padded else ""), mx),
-               "kernel": (KERNEL_NAMES_MX if mx else KERNEL_NAMES).get(dom, dom), "stage": dom,
+               "kernel": kernel_name(dom, k, mx), "stage": dom,
                "launch_ms": round(dom_ms, 4), "algorithmic_flops": fl, "algorithmic_bytes": by})
     value = T / (res["ms_per_step"] / 1e3)
     out = {
