@@ -26,6 +26,11 @@
 // Accumulation is fp32; bf16 results are rounded to nearest even.
 #include "gemm_common.h"
 
+// MFMAs issued per direct-load instruction of the next K-step
+#ifndef MOE_GEMM_LOAD_SPREAD
+#define MOE_GEMM_LOAD_SPREAD 2
+#endif
+
 namespace moe {
 namespace {
 
@@ -105,28 +110,21 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb, f
         }
     }
 
+    constexpr int NA = LA::PER_WAVE;
+    constexpr int NB = LB::PER_WAVE;
+    static_assert(NS == 2, "two LDS stages");
+    constexpr int SPREAD = MOE_GEMM_LOAD_SPREAD;   // MFMAs per load instruction
+    static_assert(NA + NB <= MI * 4 * (BK / 16) / SPREAD, "loads fit the K-step's MFMAs");
     for (int kt = 0; kt < nk; ++kt) {
-        // loads of K-steps after kt that are already in flight
-        const int ahead = min(NS - 2, nk - 1 - kt);
-        if constexpr (NS >= 4) {
-            if (ahead >= 2) wait_vmcnt<2 * PER_STEP>();
-            else if (ahead == 1) wait_vmcnt<PER_STEP>();
-            else wait_vmcnt<0>();
-        } else if constexpr (NS == 3) {
-            if (ahead >= 1) wait_vmcnt<PER_STEP>();
-            else wait_vmcnt<0>();
-        } else {
-            wait_vmcnt<0>();
-        }
-        __syncthreads();
-        if (kt + NS - 1 < nk) {
-            uint16_t* nxt = smem + ((kt + NS - 1) % NS) * STAGE;
-            la.issue(nxt, kt + NS - 1);
-            lb.issue(nxt + BM * BK, kt + NS - 1);
-        }
-        const uint16_t* a_s = smem + (kt % NS) * STAGE;
+        wait_vmcnt<0>();     // this wave's loads of K-step kt have landed
+        __syncthreads();     // everyone's have, and the other stage is no longer read
+        uint16_t* nxt = kt + 1 < nk ? smem + ((kt + 1) & 1) * STAGE : nullptr;
+        const uint16_t* a_s = smem + (kt & 1) * STAGE;
         const uint16_t* b_s = a_s + BM * BK;
-        // fragments of k-slice ks+1 are read while the MFMAs of slice ks run
+        // fragments of k-slice ks+1 are read while the MFMAs of slice ks run;
+        // the loads of K-step kt+1 go out one after every SPREAD-th MFMA, so
+        // the per-CU load path (about 64 B/clk) is not asked for more than it
+        // drains and does not stall the MFMA issue
         bf16x8 af[2][MI], bfr[2][4];
 #pragma unroll
         for (int i = 0; i < MI; ++i) af[0][i] = read_frag<BM, BK, A_MN>(a_s, wm * (BM / 2) + i * 32, 0, lane);
@@ -148,8 +146,17 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb, f
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[c][j], af[c][i], acc[i][j], 0, 0, 0);
+                    const int m = ks * MI * 4 + i * 4 + j;   // MFMA index in the K-step
+                    if (m % SPREAD == SPREAD - 1 && m / SPREAD < NA + NB && nxt) {
+                        const int q = m / SPREAD;              // load instruction index
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (q < NA) la.issue_one(nxt, kt + 1, q);
+                        else if (q < NA + NB) lb.issue_one(nxt + BM * BK, kt + 1, q - NA);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -249,8 +256,8 @@ __global__ MOE_GEMM_KERNEL_ATTRS void gemm_grouped_k_kernel(KParams p)
     const int which = local < t0 ? 0 : 1;
     if (which) local -= t0;
     const KProblem& q = p.pr[which];
-    const int mt = local / q.ntn;
-    const int nt = local - mt * q.ntn;
+    int mt, nt;
+    grouped_tile(local, q.mtn, q.ntn, 4, mt, nt);
     const int64_t g0 = group_begin(p.group_off, p.capacity, e, p.n_rows);
     const int m_e = (int)group_rows(p.group_off, p.capacity, e, p.n_rows);
 

@@ -131,6 +131,22 @@ struct DirectLoader {
             }
         }
     }
+    // instruction i (of PER_WAVE) of this wave's share of K-step kt into `tile`
+    __device__ __forceinline__ void issue_one(uint16_t* tile, int kt, int i)
+    {
+        const int w = threadIdx.x >> 6;
+        const uint32_t so = (uint32_t)kt * kstep;
+        const int q = i * 4 + w;
+        uint32_t o = off[i];
+        if (!MN && (kt + 1) * BK > K) {  // k-chunks at or past K read zero
+            const int lane = threadIdx.x & 63;
+            const int row = q * RPC_K + lane / CPR_K;
+            const int c = (int)lds_chunk<false, BK>(row, lane % CPR_K);
+            if (kt * BK + c * 8 >= K) o = kOOB;
+        }
+        const bool hi = !MN && i * 4 * RPC_K >= HALF;
+        dma_to_lds<16>(hi ? r1 : r0, tile + q * 512, o, so);
+    }
     // global -> LDS for K-step kt into the tile at `tile` (TILE_BYTES bytes)
     __device__ __forceinline__ void issue(uint16_t* tile, int kt)
     {
@@ -404,6 +420,21 @@ __device__ __forceinline__ bool schedule_m(const int32_t* group_off, int capacit
     t.row0 = g0 + (int64_t)t.mt * BM;
     t.rows_valid = min(BM, m_e - t.mt * BM);
     return true;
+}
+
+// Tile (mt, nt) of the local-th tile of an mtn x ntn grid, walked in groups
+// of GM tile rows (nt fastest across a group's columns, mt fastest within):
+// a run of consecutive tiles then shares GM row slices of A and a few column
+// slices of B, which stay in L2 while those tiles run together.
+__device__ __forceinline__ void grouped_tile(int local, int mtn, int ntn, int GM, int& mt, int& nt)
+{
+    const int per_group = GM * ntn;
+    const int g = local / per_group;
+    const int first = g * GM;
+    const int gm = min(mtn - first, GM);
+    const int r = local - g * per_group;
+    mt = first + r % gm;
+    nt = r / gm;
 }
 
 // store a BM x 256 accumulator tile as bf16 rows of C (rows [0, rows), columns

@@ -285,8 +285,8 @@ __global__ MOE_GEMM_KERNEL_ATTRS void mx_grouped_k_kernel(MxKParams p)
     const int which = local < t0 ? 0 : 1;
     if (which) local -= t0;
     const MxKProblem& q = p.pr[which];
-    const int mt = local / q.ntn;
-    const int nt = local - mt * q.ntn;
+    int mt, nt;
+    grouped_tile(local, q.mtn, q.ntn, 4, mt, nt);
     const int64_t P = (int64_t)s_pref[e] * kMxColPad;
     const int64_t Kp = (int64_t)(s_pref[e + 1] - s_pref[e]) * kMxColPad;
 
