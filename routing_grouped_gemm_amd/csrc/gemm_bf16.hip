@@ -74,25 +74,26 @@ __device__ __forceinline__ bf16x8 read_frag(const uint16_t* tile, int row_base, 
 // BM x 256 tile over s.K, accumulators acc[BM/64][4].  NS LDS stages of
 // (BM + 256) x BK bf16; the direct loads of the next NS-1 K-steps are in
 // flight while the MFMAs of the current one run; one barrier per K-step.
-template <int BM, int BK, int NS, bool A_MN, bool B_MN>
-__device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb, f32x16 (&acc)[BM / 64][4],
-                                         uint16_t* smem)
+template <int BM, int BK, int NS, bool A_MN, bool B_MN, int NW>
+__device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
+                                         f32x16 (&acc)[BM / 64][WL<NW>::NJ], uint16_t* smem)
 {
     constexpr int MI = BM / 64;
+    constexpr int NJ = WL<NW>::NJ;
     constexpr int STAGE = (BM + BN) * BK;   // elements per stage
-    using LA = DirectLoader<BM, BK, A_MN>;
-    using LB = DirectLoader<BN, BK, B_MN>;
+    using LA = DirectLoader<BM, BK, A_MN, NW>;
+    using LB = DirectLoader<BN, BK, B_MN, NW>;
     constexpr int PER_STEP = LA::PER_WAVE + LB::PER_WAVE;   // load instructions per wave per K-step
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
+    const int wm = WL<NW>::wm(wave);
+    const int wn = WL<NW>::wn(wave);
 
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -114,7 +115,7 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb, f
     constexpr int NB = LB::PER_WAVE;
     static_assert(NS == 2, "two LDS stages");
     constexpr int SPREAD = MOE_GEMM_LOAD_SPREAD;   // MFMAs per load instruction
-    static_assert(NA + NB <= MI * 4 * (BK / 16) / SPREAD, "loads fit the K-step's MFMAs");
+    static_assert(NA + NB <= MI * NJ * (BK / 16) / SPREAD, "loads fit the K-step's MFMAs");
     for (int kt = 0; kt < nk; ++kt) {
         wait_vmcnt<0>();     // this wave's loads of K-step kt have landed
         __syncthreads();     // everyone's have, and the other stage is no longer read
@@ -125,11 +126,11 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb, f
         // the loads of K-step kt+1 go out one after every SPREAD-th MFMA, so
         // the per-CU load path (about 64 B/clk) is not asked for more than it
         // drains and does not stall the MFMA issue
-        bf16x8 af[2][MI], bfr[2][4];
+        bf16x8 af[2][MI], bfr[2][NJ];
 #pragma unroll
         for (int i = 0; i < MI; ++i) af[0][i] = read_frag<BM, BK, A_MN>(a_s, wm * (BM / 2) + i * 32, 0, lane);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bfr[0][j] = read_frag<BN, BK, B_MN>(b_s, sub_col(wn, j), 0, lane);
+        for (int j = 0; j < NJ; ++j) bfr[0][j] = read_frag<BN, BK, B_MN>(b_s, WL<NW>::sub_col(wn, j), 0, lane);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             const int c = ks & 1;
@@ -138,17 +139,17 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb, f
                 for (int i = 0; i < MI; ++i)
                     af[c ^ 1][i] = read_frag<BM, BK, A_MN>(a_s, wm * (BM / 2) + i * 32, ks + 1, lane);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    bfr[c ^ 1][j] = read_frag<BN, BK, B_MN>(b_s, sub_col(wn, j), ks + 1, lane);
+                for (int j = 0; j < NJ; ++j)
+                    bfr[c ^ 1][j] = read_frag<BN, BK, B_MN>(b_s, WL<NW>::sub_col(wn, j), ks + 1, lane);
             }
             // keep the reads of slice ks+1 ahead of the MFMAs of slice ks
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < NJ; ++j) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[c][j], af[c][i], acc[i][j], 0, 0, 0);
-                    const int m = ks * MI * 4 + i * 4 + j;   // MFMA index in the K-step
+                    const int m = ks * MI * NJ + i * NJ + j;   // MFMA index in the K-step
                     if (m % SPREAD == SPREAD - 1 && m / SPREAD < NA + NB && nxt) {
                         const int q = m / SPREAD;              // load instruction index
                         __builtin_amdgcn_sched_barrier(0);
@@ -165,16 +166,16 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb, f
 
 // Grouped-M GEMM: C[rows of group e] = A[rows of group e] x B_e^T (B_MN = false:
 // B_e stored [N, K]) or A x B_e (B_MN = true: B_e stored [K, N]).
-template <int BM, int BK, int NS, bool B_MN, int EPI>
-__global__ MOE_GEMM_KERNEL_ATTRS void gemm_grouped_m_kernel(MParams p)
+template <int BM, int BK, int NS, bool B_MN, int EPI, int NW>
+__global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_m_kernel(MParams p)
 {
     __shared__ __align__(16) uint16_t smem[NS * (BM + BN) * BK];
     __shared__ int s_pref[kMaxExperts + 1];
-    __shared__ int s_part[NTH];
+    __shared__ int s_part[64 * NW];
 
     // device tile schedule: expert-major, N-tile, then M-tile
     MTile tile;
-    if (!schedule_m<BM, NTH>(p.group_off, p.capacity, p.E, p.n_rows, p.ntn, s_pref, s_part, tile)) return;
+    if (!schedule_m<BM, 64 * NW>(p.group_off, p.capacity, p.E, p.n_rows, p.ntn, s_pref, s_part, tile)) return;
     const int e = tile.e, nt = tile.nt;
     const int64_t row0 = tile.row0;
     const int rows_valid = tile.rows_valid;
@@ -209,9 +210,9 @@ __global__ MOE_GEMM_KERNEL_ATTRS void gemm_grouped_m_kernel(MParams p)
         sb.rows1 = max(min(128, p.N - n0 - 128), 0);
     }
 
-    f32x16 acc[BM / 64][4];
-    mainloop<BM, BK, NS, false, B_MN>(sa, sb, acc, smem);
-    epilogue_m<BM, EPI>(acc, p, row0, rows_valid, nt, reinterpret_cast<uint8_t*>(smem));
+    f32x16 acc[BM / 64][WL<NW>::NJ];
+    mainloop<BM, BK, NS, false, B_MN, NW>(sa, sb, acc, smem);
+    epilogue_m<BM, EPI, NW>(acc, p, row0, rows_valid, nt, reinterpret_cast<uint8_t*>(smem));
 }
 
 
@@ -238,8 +239,8 @@ struct KParams {
 // Grouped-K GEMM (weight gradients): C_e = A_e^T B_e over the rows of group e,
 // for one or two problems sharing the groups.  Tiles are expert-major so the
 // tiles reading one expert's rows run together on one XCD.
-template <int BM, int BK, int NS>
-__global__ MOE_GEMM_KERNEL_ATTRS void gemm_grouped_k_kernel(KParams p)
+template <int BM, int BK, int NS, int NW>
+__global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_kernel(KParams p)
 {
     __shared__ __align__(16) uint16_t smem[NS * (BM + BN) * BK];
     const int t0 = p.pr[0].mtn * p.pr[0].ntn;
@@ -274,26 +275,26 @@ __global__ MOE_GEMM_KERNEL_ATTRS void gemm_grouped_k_kernel(KParams p)
     sb.rows1 = 0;
     sb.K = m_e;
 
-    f32x16 acc[BM / 64][4];
-    mainloop<BM, BK, NS, true, true>(sa, sb, acc, smem);
+    f32x16 acc[BM / 64][WL<NW>::NJ];
+    mainloop<BM, BK, NS, true, true, NW>(sa, sb, acc, smem);
 
-    store_tile<BM>(acc, q.C + (int64_t)e * q.sC + (int64_t)mt * BM * q.ldc, q.ldc, q.M - mt * BM, nt * BN,
+    store_tile<BM, NW>(acc, q.C + (int64_t)e * q.sC + (int64_t)mt * BM * q.ldc, q.ldc, q.M - mt * BM, nt * BN,
                    q.N, reinterpret_cast<uint8_t*>(smem));
 }
 
-template <int BM, int BK, int NS, bool B_MN, int EPI>
+template <int BM, int BK, int NS, bool B_MN, int EPI, int NW>
 hipError_t launch_m(const MParams& p, int64_t n_rows, hipStream_t s)
 {
     // host-known bound on the M-tiles: sum ceil(m_e / BM) <= n_rows / BM + E
     const int64_t bound = (n_rows / BM + p.E) * (int64_t)p.ntn;
     const int64_t grid = (bound + 7) / 8 * 8;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_grouped_m_kernel<BM, BK, NS, B_MN, EPI>), dim3((unsigned)grid), dim3(NTH), 0,
-                       s, p);
+    hipLaunchKernelGGL((gemm_grouped_m_kernel<BM, BK, NS, B_MN, EPI, NW>), dim3((unsigned)grid), dim3(64 * NW),
+                       0, s, p);
     return hipGetLastError();
 }
 
-template <int BM, int BK, int NS>
+template <int BM, int BK, int NS, int NW>
 hipError_t launch_k(const KParams& p, hipStream_t s)
 {
     int64_t tiles_e = 0;
@@ -301,7 +302,7 @@ hipError_t launch_k(const KParams& p, hipStream_t s)
     const int64_t total = (int64_t)p.E * tiles_e;
     const int64_t grid = (total + 7) / 8 * 8;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_grouped_k_kernel<BM, BK, NS>), dim3((unsigned)grid), dim3(NTH), 0, s, p);
+    hipLaunchKernelGGL((gemm_grouped_k_kernel<BM, BK, NS, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
     return hipGetLastError();
 }
 
@@ -321,6 +322,10 @@ constexpr int kBM = MOE_GEMM_BM_M;   // M tile of the grouped-M (forward / dgrad
 constexpr int kBMK = MOE_GEMM_BM_K;  // M tile of the grouped-K (weight gradient) GEMM
 constexpr int kBK = MOE_GEMM_BK;     // K step
 constexpr int kNS = MOE_GEMM_NS;     // LDS pipeline stages
+#ifndef MOE_GEMM_WAVES
+#define MOE_GEMM_WAVES 8
+#endif
+constexpr int kNW = MOE_GEMM_WAVES;  // waves per workgroup (4: one per SIMD, 8: two)
 
 }  // namespace
 
@@ -347,7 +352,7 @@ hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, i
         p.ldc = 2 * f;
         p.H = (uint16_t*)t.h;
         p.ldh = f;
-        return launch_m<kBM, kBK, kNS, false, EPI_SWIGLU_FWD>(p, g.n_rows, s);
+        return launch_m<kBM, kBK, kNS, false, EPI_SWIGLU_FWD, kNW>(p, g.n_rows, s);
     case MOE_GEMM_DOWN:  // y = h Wd^T
         p.A = (const uint16_t*)t.h;
         p.lda = f;
@@ -359,7 +364,7 @@ hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, i
         p.ntn = (d + BN - 1) / BN;
         p.C = (uint16_t*)t.y_perm;
         p.ldc = d;
-        return launch_m<kBM, kBK, kNS, false, EPI_STORE>(p, g.n_rows, s);
+        return launch_m<kBM, kBK, kNS, false, EPI_STORE, kNW>(p, g.n_rows, s);
     case MOE_GEMM_DGRAD_DOWN:  // dh = dy Wd (Wd_e stored [d, f] = [K, N]), SwiGLU backward
         p.A = (const uint16_t*)t.dy_perm;
         p.lda = d;
@@ -373,7 +378,7 @@ hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, i
         p.ldc = 2 * f;
         p.G = (const uint16_t*)t.gu;
         p.ldg = 2 * f;
-        return launch_m<kBM, kBK, kNS, true, EPI_SWIGLU_BWD>(p, g.n_rows, s);
+        return launch_m<kBM, kBK, kNS, true, EPI_SWIGLU_BWD, kNW>(p, g.n_rows, s);
     case MOE_GEMM_DGRAD_GATE_UP:  // dx = [dg | du] [Wg ; Wu] (W13_e stored [2f, d] = [K, N])
         p.A = (const uint16_t*)t.dgu;
         p.lda = 2 * f;
@@ -385,7 +390,7 @@ hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, i
         p.ntn = (d + BN - 1) / BN;
         p.C = (uint16_t*)t.dx_perm;
         p.ldc = d;
-        return launch_m<kBM, kBK, kNS, true, EPI_STORE>(p, g.n_rows, s);
+        return launch_m<kBM, kBK, kNS, true, EPI_STORE, kNW>(p, g.n_rows, s);
     case MOE_GEMM_WGRAD: {  // dWd_e [d, f] = dy_e^T h_e ; dW13_e [2f, d] = dgu_e^T x_e
         KParams k{};
         k.group_off = g.group_off;
@@ -417,7 +422,7 @@ hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, i
         b.C = (uint16_t*)t.dw13;
         b.ldc = d;
         b.sC = (int64_t)2 * f * d;
-        return launch_k<kBMK, kBK, kNS>(k, s);
+        return launch_k<kBMK, kBK, kNS, kNW>(k, s);
     }
     default:
         return hipErrorInvalidValue;

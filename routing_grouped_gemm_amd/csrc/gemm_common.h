@@ -89,10 +89,10 @@ __device__ __forceinline__ uint32_t lds_chunk(int row_or_k, int c)
     else return (uint32_t)(c ^ ((row_or_k >> 2) & 3));
 }
 
-template <int ROWS, int BK, bool MN>
+template <int ROWS, int BK, bool MN, int NW = 4>
 struct DirectLoader {
     static constexpr int TILE_BYTES = ROWS * BK * 2;
-    static constexpr int PER_WAVE = TILE_BYTES / 1024 / 4;   // 1 KB instructions per wave per K-step
+    static constexpr int PER_WAVE = TILE_BYTES / 1024 / NW;  // 1 KB instructions per wave per K-step
     static constexpr int HALF = ROWS / 2;
     static constexpr int CPR_K = BK / 8;                     // 16-byte chunks per K-major row
     static constexpr int RPC_K = 1024 / (BK * 2);            // K-major rows per 1 KB chunk
@@ -111,7 +111,7 @@ struct DirectLoader {
             kstep = BK * 2;
 #pragma unroll
             for (int i = 0; i < PER_WAVE; ++i) {
-                const int q = i * 4 + w;
+                const int q = i * NW + w;
                 const int row = q * RPC_K + lane / CPR_K;
                 const int c = (int)lds_chunk<false, BK>(row, lane % CPR_K);   // XOR is an involution
                 const int rr = row >= HALF ? row - HALF : row;
@@ -124,7 +124,7 @@ struct DirectLoader {
             constexpr int CPR = ROWS / 8;              // 16-byte chunks per k-row
 #pragma unroll
             for (int i = 0; i < PER_WAVE; ++i) {
-                const int q = i * 4 + w;
+                const int q = i * NW + w;
                 const int k = q * KROWS + lane / CPR;
                 const int c = (int)lds_chunk<true, BK>(k, lane % CPR);
                 off[i] = c * 8 < s.rows0 ? (uint32_t)(k * s.ld * 2 + c * 16) : kOOB;
@@ -136,7 +136,7 @@ struct DirectLoader {
     {
         const int w = threadIdx.x >> 6;
         const uint32_t so = (uint32_t)kt * kstep;
-        const int q = i * 4 + w;
+        const int q = i * NW + w;
         uint32_t o = off[i];
         if (!MN && (kt + 1) * BK > K) {  // k-chunks at or past K read zero
             const int lane = threadIdx.x & 63;
@@ -144,29 +144,14 @@ struct DirectLoader {
             const int c = (int)lds_chunk<false, BK>(row, lane % CPR_K);
             if (kt * BK + c * 8 >= K) o = kOOB;
         }
-        const bool hi = !MN && i * 4 * RPC_K >= HALF;
+        const bool hi = !MN && i * NW * RPC_K >= HALF;
         dma_to_lds<16>(hi ? r1 : r0, tile + q * 512, o, so);
     }
     // global -> LDS for K-step kt into the tile at `tile` (TILE_BYTES bytes)
     __device__ __forceinline__ void issue(uint16_t* tile, int kt)
     {
-        const int w = threadIdx.x >> 6;
-        const uint32_t so = (uint32_t)kt * kstep;
-        const bool ktail = !MN && (kt + 1) * BK > K;
 #pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) {
-            const int q = i * 4 + w;
-            uint32_t o = off[i];
-            if (ktail) {  // k-chunks at or past K read zero
-                const int lane = threadIdx.x & 63;
-                const int row = q * RPC_K + lane / CPR_K;
-                const int c = (int)lds_chunk<false, BK>(row, lane % CPR_K);
-                if (kt * BK + c * 8 >= K) o = kOOB;
-            }
-            // row block of this instruction: rows [q*RPC_K, ...) lie in the upper half iff q*RPC_K >= HALF
-            const bool hi = !MN && i * 4 * RPC_K >= HALF;
-            dma_to_lds<16>(hi ? r1 : r0, tile + q * 512, o, so);
-        }
+        for (int i = 0; i < PER_WAVE; ++i) issue_one(tile, kt, i);
     }
 };
 
@@ -175,17 +160,34 @@ struct DirectLoader {
 __device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 __device__ __forceinline__ float silu_f(float g) { return g * sigmoid_f(g); }
 
-// first column (0..255) of the 32-wide sub-tile j of wave column wn
-__device__ __forceinline__ int sub_col(int wn, int j) { return (j >> 1) * 128 + wn * 64 + (j & 1) * 32; }
+// Wave layout of a BM x 256 output tile.  NW = 4: 2 x 2 waves of (BM/2) x
+// 128, sub-tiles j = 0..3 at columns (j>>1)*128 + wn*64 + (j&1)*32.  NW = 8
+// (two waves per SIMD): 2 x 4 waves of (BM/2) x 64, sub-tiles j = 0..1 at
+// columns j*128 + wn*32.  Either way sub-tiles j and j + NJ/2 of a wave are
+// the same columns of the two 128-column halves of the tile (the gate and up
+// columns of the SwiGLU forward).
+template <int NW>
+struct WL {
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+    static constexpr int NJ = NW == 4 ? 4 : 2;   // 32-column sub-tiles per wave
+    static constexpr int NT = 64 * NW;           // threads
+    __device__ static int wm(int wave) { return NW == 4 ? wave >> 1 : wave >> 2; }
+    __device__ static int wn(int wave) { return NW == 4 ? wave & 1 : wave & 3; }
+    __device__ static int sub_col(int wn, int j) { return NW == 4 ? (j >> 1) * 128 + wn * 64 + (j & 1) * 32 : j * 128 + wn * 32; }
+};
+
+// first column (0..255) of the 32-wide sub-tile j of wave column wn (4 waves)
+__device__ __forceinline__ int sub_col(int wn, int j) { return WL<4>::sub_col(wn, j); }
 
 // Accumulator layout.  The MFMA is issued with the B fragment as its first
 // operand, so acc[i][j] holds the transpose of sub-tile (i, j): lane l owns
 // tile row  wm*(BM/2) + 32*i + (l & 31)  and, for g = 0..3, the four
 // consecutive columns  sub_col(wn, j) + 8*g + 4*(l >> 5) + {0,1,2,3}  in
 // acc[i][j][4g .. 4g+3].
+template <int NW = 4>
 __device__ __forceinline__ int acc_col(int wn, int j, int g, int lane)
 {
-    return sub_col(wn, j) + 8 * g + 4 * (lane >> 5);
+    return WL<NW>::sub_col(wn, j) + 8 * g + 4 * (lane >> 5);
 }
 
 __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d)
@@ -252,12 +254,12 @@ __device__ __forceinline__ void stage_put(uint8_t* lds, uint32_t off, uint2 v)
 
 // After a barrier: thread t hands out chunks t, t + NTH, ... as put(r, c, v);
 // a trailing barrier frees the LDS again.
-template <int ROWS, int CH, class F>
+template <int ROWS, int CH, int NT = NTH, class F>
 __device__ __forceinline__ void stage_flush(const uint8_t* lds, F&& put)
 {
     __syncthreads();
 #pragma unroll 4
-    for (int q = threadIdx.x; q < ROWS * CH; q += NTH) {
+    for (int q = threadIdx.x; q < ROWS * CH; q += NT) {
         const int r = q / CH, c = q % CH;
         put(r, c, *reinterpret_cast<const uint4*>(lds + r * (CH * 16) + ((c ^ (r & (CH - 1))) << 4)));
     }
@@ -265,41 +267,43 @@ __device__ __forceinline__ void stage_flush(const uint8_t* lds, F&& put)
 }
 
 // the accumulator tile (BM x 256) as bf16 into the staging layout
-template <int BM>
-__device__ __forceinline__ void stage_acc(const f32x16 (&acc)[BM / 64][4], uint8_t* lds)
+template <int BM, int NW = 4>
+__device__ __forceinline__ void stage_acc(const f32x16 (&acc)[BM / 64][WL<NW>::NJ], uint8_t* lds)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = WL<NW>::wm(wave), wn = WL<NW>::wn(wave);
 #pragma unroll
     for (int i = 0; i < BM / 64; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < WL<NW>::NJ; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                stage_put(lds, stage_off<32>(wm * (BM / 2) + i * 32 + (lane & 31), acc_col(wn, j, g, lane)),
+                stage_put(lds, stage_off<32>(wm * (BM / 2) + i * 32 + (lane & 31), acc_col<NW>(wn, j, g, lane)),
                           pack4_bf16(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                                      acc[i][j][4 * g + 3]));
 }
 
-template <int BM, int EPI>
-__device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][4], const MParams& p,
+template <int BM, int EPI, int NW = 4>
+__device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][WL<NW>::NJ], const MParams& p,
                                            int64_t row0, int rows_valid, int nt, uint8_t* lds)
 {
     constexpr int MI = BM / 64;
+    constexpr int NJ = WL<NW>::NJ;
+    constexpr int NT = WL<NW>::NT;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int lane = threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = WL<NW>::wm(wave), wn = WL<NW>::wn(wave);
     if constexpr (EPI == EPI_STORE) {
-        stage_acc<BM>(acc, lds);
-        stage_flush<BM, 32>(lds, [&](int r, int c, uint4 v) {
+        stage_acc<BM, NW>(acc, lds);
+        stage_flush<BM, 32, NT>(lds, [&](int r, int c, uint4 v) {
             const int n = nt * BN + 8 * c;
             if (r < rows_valid && n < p.N) *reinterpret_cast<uint4*>(p.C + (row0 + r) * p.ldc + n) = v;
         });
     } else if constexpr (EPI == EPI_SWIGLU_FWD) {
         // tile columns 0..127 are gate columns n0.., 128..255 the up columns f + n0..
         const int n0 = nt * 128;
-        stage_acc<BM>(acc, lds);
-        stage_flush<BM, 32>(lds, [&](int r, int c, uint4 v) {
+        stage_acc<BM, NW>(acc, lds);
+        stage_flush<BM, 32, NT>(lds, [&](int r, int c, uint4 v) {
             const int n = n0 + 8 * (c & 15);
             if (r < rows_valid && n < p.f)
                 *reinterpret_cast<uint4*>(p.C + (row0 + r) * p.ldc + (c < 16 ? n : p.f + n)) = v;
@@ -308,16 +312,16 @@ __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][4], cons
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < NJ / 2; ++j)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     float hv[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) hv[q] = silu_f(acc[i][j][4 * g + q]) * acc[i][j + 2][4 * g + q];
-                    stage_put(lds, stage_off<16>(wm * (BM / 2) + i * 32 + (lane & 31), acc_col(wn, j, g, lane)),
+                    for (int q = 0; q < 4; ++q) hv[q] = silu_f(acc[i][j][4 * g + q]) * acc[i][j + NJ / 2][4 * g + q];
+                    stage_put(lds, stage_off<16>(wm * (BM / 2) + i * 32 + (lane & 31), acc_col<NW>(wn, j, g, lane)),
                               pack4_bf16(hv[0], hv[1], hv[2], hv[3]));
                 }
-        stage_flush<BM, 16>(lds, [&](int r, int c, uint4 v) {
+        stage_flush<BM, 16, NT>(lds, [&](int r, int c, uint4 v) {
             const int n = n0 + 8 * c;
             if (r < rows_valid && n < p.f) *reinterpret_cast<uint4*>(p.H + (row0 + r) * p.ldh + n) = v;
         });
@@ -336,8 +340,8 @@ __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][4], cons
         for (int ch = 0; ch < 2; ++ch) {
             const int nc = n0 + 128 * ch;                   // first column of this half
 #pragma unroll
-            for (int i = 0; i < QTILE / 1024 / 4; ++i) {
-                const int q = i * 4 + wave;                 // 1 KB slice of the tile
+            for (int i = 0; i < QTILE / 1024 / NW; ++i) {
+                const int q = i * NW + wave;                // 1 KB slice of the tile
                 const int slot = q * 64 + lane;             // 16-byte staging slot
                 const int r = slot >> 4, c = (slot & 15) ^ (r & 15);
                 const uint32_t off = (uint32_t)((r * p.ldg + nc + 8 * c) * 2);
@@ -349,12 +353,12 @@ __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][4], cons
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
+                for (int jj = 0; jj < NJ / 2; ++jj)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        const int j = 2 * ch + jj;
+                        const int j = (NJ / 2) * ch + jj;
                         const uint32_t off = stage_off<16>(wm * (BM / 2) + i * 32 + (lane & 31),
-                                                           acc_col(wn, j, g, lane) - 128 * ch);
+                                                           acc_col<NW>(wn, j, g, lane) - 128 * ch);
                         float gv[4], uv[4], dgv[4], duv[4];
                         unpack4_bf16(*reinterpret_cast<const uint2*>(lg + off), gv);
                         unpack4_bf16(*reinterpret_cast<const uint2*>(lu + off), uv);
@@ -370,7 +374,7 @@ __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][4], cons
                     }
             __syncthreads();
 #pragma unroll 4
-            for (int q = threadIdx.x; q < BM * 16 * 2; q += NTH) {
+            for (int q = threadIdx.x; q < BM * 16 * 2; q += NT) {
                 const int which = q / (BM * 16), qq = q % (BM * 16);
                 const int r = qq >> 4, c = qq & 15;
                 const int n = nc + 8 * c;
@@ -387,6 +391,10 @@ __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][4], cons
 // whole register file (accumulators in AGPRs)
 #define MOE_GEMM_KERNEL_ATTRS \
     __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(1, 1), amdgpu_flat_work_group_size(NTH, NTH)))
+// NW waves: NW / 4 per SIMD, each with the register file share that allows
+#define MOE_GEMM_KERNEL_ATTRS_NW(NW) \
+    __launch_bounds__(64 * (NW)) __attribute__((amdgpu_waves_per_eu((NW) / 4, (NW) / 4), \
+                                               amdgpu_flat_work_group_size(64 * (NW), 64 * (NW))))
 
 
 // Device tile schedule of a grouped-M launch: every workgroup builds the
@@ -439,12 +447,12 @@ __device__ __forceinline__ void grouped_tile(int local, int mtn, int ntn, int GM
 
 // store a BM x 256 accumulator tile as bf16 rows of C (rows [0, rows), columns
 // col0 + [0, 256) below N), through the LDS staging above
-template <int BM>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[BM / 64][4], uint16_t* C, int64_t ldc,
+template <int BM, int NW = 4>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[BM / 64][WL<NW>::NJ], uint16_t* C, int64_t ldc,
                                            int rows, int col0, int N, uint8_t* lds)
 {
-    stage_acc<BM>(acc, lds);
-    stage_flush<BM, 32>(lds, [&](int r, int c, uint4 v) {
+    stage_acc<BM, NW>(acc, lds);
+    stage_flush<BM, 32, WL<NW>::NT>(lds, [&](int r, int c, uint4 v) {
         const int n = col0 + 8 * c;
         if (r < rows && n < N) *reinterpret_cast<uint4*>(C + r * ldc + n) = v;
     });
