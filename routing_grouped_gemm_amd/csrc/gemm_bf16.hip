@@ -24,6 +24,8 @@
 //     formed in registers and g, u, h are stored); the SwiGLU backward (reads
 //     the saved g, u of its elements and stores dg, du).
 // Accumulation is fp32; bf16 results are rounded to nearest even.
+#include <type_traits>
+
 #include "gemm_common.h"
 
 // MFMAs issued per direct-load instruction of the next K-step
@@ -71,19 +73,29 @@ __device__ __forceinline__ bf16x8 read_frag(const uint16_t* tile, int row_base, 
     }
 }
 
-// BM x 256 tile over s.K, accumulators acc[BM/64][4].  NS LDS stages of
-// (BM + 256) x BK bf16; the direct loads of the next NS-1 K-steps are in
-// flight while the MFMAs of the current one run; one barrier per K-step.
-template <int BM, int BK, int NS, bool A_MN, bool B_MN, int NW>
+// BM x 256 tile over s.K, accumulators acc[BM/64][NJ].  Two LDS stages of
+// (BM + 256) x BK bf16: the direct loads of K-step kt+1 are in flight while
+// the MFMAs of K-step kt run; one barrier per K-step.  Fragments of k-slice
+// ks+1 are read while the MFMAs of slice ks run, and the MFMAs of each
+// K-step's last slice are issued after the next barrier, so that they cover
+// the latency of the first fragment reads of the new K-step.
+template <int BM, int BK, int NS, bool A_MN, bool B_MN, int NW, bool KAL>
 __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
                                          f32x16 (&acc)[BM / 64][WL<NW>::NJ], uint16_t* smem)
 {
     constexpr int MI = BM / 64;
     constexpr int NJ = WL<NW>::NJ;
+    constexpr int KS = BK / 16;             // k-slices per K-step
     constexpr int STAGE = (BM + BN) * BK;   // elements per stage
     using LA = DirectLoader<BM, BK, A_MN, NW>;
     using LB = DirectLoader<BN, BK, B_MN, NW>;
-    constexpr int PER_STEP = LA::PER_WAVE + LB::PER_WAVE;   // load instructions per wave per K-step
+    constexpr int NA = LA::PER_WAVE;
+    constexpr int NB = LB::PER_WAVE;
+    constexpr int SPREAD = MOE_GEMM_LOAD_SPREAD;   // MFMAs per load instruction
+    constexpr int QPS = MI * NJ / SPREAD;          // load instructions per k-slice of MFMAs
+    static_assert(NS == 2, "two LDS stages");
+    static_assert(KS >= 2 && KS % 2 == 0, "an even number of k-slices per K-step");
+    static_assert(NA + NB <= 2 * QPS, "the loads fit the MFMAs of two k-slices");
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -101,72 +113,87 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
     if (nk == 0) return;
     LA la;
     LB lb;
-    la.init(sa);
-    lb.init(sb);
-#pragma unroll
-    for (int st = 0; st < NS - 1; ++st) {
-        if (st < nk) {
-            la.issue(smem + st * STAGE, st);
-            lb.issue(smem + st * STAGE + BM * BK, st);
-        }
-    }
+    la.init(sa, lds_addr(smem));
+    lb.init(sb, lds_addr(smem + BM * BK));
+    la.issue(smem, 0);
+    lb.issue(smem + BM * BK, 0);
 
-    constexpr int NA = LA::PER_WAVE;
-    constexpr int NB = LB::PER_WAVE;
-    static_assert(NS == 2, "two LDS stages");
-    constexpr int SPREAD = MOE_GEMM_LOAD_SPREAD;   // MFMAs per load instruction
-    static_assert(NA + NB <= MI * NJ * (BK / 16) / SPREAD, "loads fit the K-step's MFMAs");
-    for (int kt = 0; kt < nk; ++kt) {
+    bf16x8 af[2][MI], bfr[2][NJ];
+    auto read = [&](int buf, const uint16_t* a_s, const uint16_t* b_s, int ks) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i) af[buf][i] = read_frag<BM, BK, A_MN>(a_s, wm * (BM / 2) + i * 32, ks, lane);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) bfr[buf][j] = read_frag<BN, BK, B_MN>(b_s, WL<NW>::sub_col(wn, j), ks, lane);
+    };
+    // the MFMAs of one k-slice from fragment buffer buf; load instruction
+    // q0 + m / SPREAD goes out after the m-th MFMA when m % SPREAD == SPREAD-1
+    auto slice = [&](int buf, int q0, auto&& load) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][j], af[buf][i], acc[i][j], 0, 0, 0);
+                const int m = i * NJ + j;
+                if (m % SPREAD == SPREAD - 1 && q0 + m / SPREAD < NA + NB) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    load(q0 + m / SPREAD);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+    };
+
+    // one K-step.  MODE 1: the next K-step lies inside K (or is masked past K
+    // by the descriptors), so its loads go out without the K-tail test;
+    // 2: loads with the K-tail test, if there is a next K-step; 0: no loads
+    auto kstep = [&](int kt, auto MODE) __attribute__((always_inline)) {
+        constexpr int md = decltype(MODE)::value;
         wait_vmcnt<0>();     // this wave's loads of K-step kt have landed
         __syncthreads();     // everyone's have, and the other stage is no longer read
-        uint16_t* nxt = kt + 1 < nk ? smem + ((kt + 1) & 1) * STAGE : nullptr;
         const uint16_t* a_s = smem + (kt & 1) * STAGE;
         const uint16_t* b_s = a_s + BM * BK;
-        // fragments of k-slice ks+1 are read while the MFMAs of slice ks run;
-        // the loads of K-step kt+1 go out one after every SPREAD-th MFMA, so
-        // the per-CU load path (about 64 B/clk) is not asked for more than it
-        // drains and does not stall the MFMA issue
-        bf16x8 af[2][MI], bfr[2][NJ];
-#pragma unroll
-        for (int i = 0; i < MI; ++i) af[0][i] = read_frag<BM, BK, A_MN>(a_s, wm * (BM / 2) + i * 32, 0, lane);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) bfr[0][j] = read_frag<BN, BK, B_MN>(b_s, WL<NW>::sub_col(wn, j), 0, lane);
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int c = ks & 1;
-            if (ks + 1 < BK / 16) {
-#pragma unroll
-                for (int i = 0; i < MI; ++i)
-                    af[c ^ 1][i] = read_frag<BM, BK, A_MN>(a_s, wm * (BM / 2) + i * 32, ks + 1, lane);
-#pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                    bfr[c ^ 1][j] = read_frag<BN, BK, B_MN>(b_s, WL<NW>::sub_col(wn, j), ks + 1, lane);
+        const uint32_t nso = (uint32_t)(((kt + 1) & 1) * STAGE * 2);   // next stage, bytes
+        auto load = [&](int q) __attribute__((always_inline)) {
+            if constexpr (md == 1) {
+                if (q < NA) la.issue_fast(nso, kt + 1, q);
+                else lb.issue_fast(nso, kt + 1, q - NA);
+            } else if (md == 2 && kt + 1 < nk) {
+                uint16_t* nxt = smem + ((kt + 1) & 1) * STAGE;
+                if (q < NA) la.issue_one(nxt, kt + 1, q);
+                else lb.issue_one(nxt + BM * BK, kt + 1, q - NA);
             }
-            // keep the reads of slice ks+1 ahead of the MFMAs of slice ks
+        };
+        read(0, a_s, b_s, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt > 0) {
+            slice(1, 0, load);   // the last k-slice of K-step kt-1
+        } else {
+#pragma unroll
+            for (int q = 0; q < QPS && q < NA + NB; ++q) load(q);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks + 1 < KS; ++ks) {
+            read((ks + 1) & 1, a_s, b_s, ks + 1);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[c][j], af[c][i], acc[i][j], 0, 0, 0);
-                    const int m = ks * MI * NJ + i * NJ + j;   // MFMA index in the K-step
-                    if (m % SPREAD == SPREAD - 1 && m / SPREAD < NA + NB && nxt) {
-                        const int q = m / SPREAD;              // load instruction index
-                        __builtin_amdgcn_sched_barrier(0);
-                        if (q < NA) la.issue_one(nxt, kt + 1, q);
-                        else if (q < NA + NB) lb.issue_one(nxt + BM * BK, kt + 1, q - NA);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
+            slice(ks & 1, (ks + 1) * QPS, load);
             __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    // KAL: K is a multiple of BK (or both operands are MN-major), so every
+    // next K-step lies inside K
+    if constexpr (KAL || (A_MN && B_MN)) {
+        for (int kt = 0; kt + 1 < nk; ++kt) kstep(kt, std::integral_constant<int, 1>{});
+        kstep(nk - 1, std::integral_constant<int, 0>{});
+    } else {
+        for (int kt = 0; kt < nk; ++kt) kstep(kt, std::integral_constant<int, 2>{});
     }
+    slice(1, NA + NB, [](int) __attribute__((always_inline)) {});   // the last k-slice of the last K-step
     __syncthreads();  // the LDS may be reused by the caller
 }
 
 // Grouped-M GEMM: C[rows of group e] = A[rows of group e] x B_e^T (B_MN = false:
 // B_e stored [N, K]) or A x B_e (B_MN = true: B_e stored [K, N]).
-template <int BM, int BK, int NS, bool B_MN, int EPI, int NW>
+template <int BM, int BK, int NS, bool B_MN, int EPI, int NW, bool KAL>
 __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_m_kernel(MParams p)
 {
     __shared__ __align__(16) uint16_t smem[NS * (BM + BN) * BK];
@@ -211,7 +238,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_m_kernel(MParams p)
     }
 
     f32x16 acc[BM / 64][WL<NW>::NJ];
-    mainloop<BM, BK, NS, false, B_MN, NW>(sa, sb, acc, smem);
+    mainloop<BM, BK, NS, false, B_MN, NW, KAL>(sa, sb, acc, smem);
     epilogue_m<BM, EPI, NW>(acc, p, row0, rows_valid, nt, reinterpret_cast<uint8_t*>(smem));
 }
 
@@ -276,7 +303,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_kernel(KParams p)
     sb.K = m_e;
 
     f32x16 acc[BM / 64][WL<NW>::NJ];
-    mainloop<BM, BK, NS, true, true, NW>(sa, sb, acc, smem);
+    mainloop<BM, BK, NS, true, true, NW, true>(sa, sb, acc, smem);
 
     store_tile<BM, NW>(acc, q.C + (int64_t)e * q.sC + (int64_t)mt * BM * q.ldc, q.ldc, q.M - mt * BM, nt * BN,
                    q.N, reinterpret_cast<uint8_t*>(smem));
@@ -289,8 +316,13 @@ hipError_t launch_m(const MParams& p, int64_t n_rows, hipStream_t s)
     const int64_t bound = (n_rows / BM + p.E) * (int64_t)p.ntn;
     const int64_t grid = (bound + 7) / 8 * 8;
     if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_grouped_m_kernel<BM, BK, NS, B_MN, EPI, NW>), dim3((unsigned)grid), dim3(64 * NW),
-                       0, s, p);
+    // K a multiple of BK: the main loop needs no K-tail tests
+    if (p.K % BK == 0)
+        hipLaunchKernelGGL((gemm_grouped_m_kernel<BM, BK, NS, B_MN, EPI, NW, true>), dim3((unsigned)grid),
+                           dim3(64 * NW), 0, s, p);
+    else
+        hipLaunchKernelGGL((gemm_grouped_m_kernel<BM, BK, NS, B_MN, EPI, NW, false>), dim3((unsigned)grid),
+                           dim3(64 * NW), 0, s, p);
     return hipGetLastError();
 }
 

@@ -59,6 +59,21 @@ __device__ __forceinline__ void dma_to_lds(desc_t desc, const void* lds, uint32_
                      :: "s"(base), "v"(voff), "s"(desc), "s"(soff) : "memory");
 }
 
+// LDS byte address of a pointer into shared memory, as a wave-uniform value
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    const auto lp = (__attribute__((address_space(3))) const void*)p;
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lp);
+}
+
+// dma_to_lds<16> with the LDS destination given as a wave-uniform byte
+// address (no pointer conversion at the issue point)
+__device__ __forceinline__ void dma16_to_lds_at(desc_t desc, uint32_t lds, uint32_t voff, uint32_t soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(voff), "s"(desc), "s"(soff) : "memory");
+}
+
 // A ROWS x BK tile source.  K-major: element (r, k) at p[r*ld + k], rows split
 // into two halves with their own bases and valid counts.  MN-major: element
 // (r, k) at p[k*ld + r] with rows0 valid rows.
@@ -99,12 +114,14 @@ struct DirectLoader {
     desc_t r0, r1;
     uint32_t off[PER_WAVE];   // per-lane byte offset of its element at k = 0
     uint32_t kstep;           // bytes a K-step advances (scalar)
+    uint32_t m0w;             // LDS byte address of this wave's first 1 KB chunk in the stage-0 tile
     int K;
-    __device__ __forceinline__ void init(const TileSrc& s)
+    __device__ __forceinline__ void init(const TileSrc& s, uint32_t lds_tile = 0)
     {
         const int lane = threadIdx.x & 63;
         const int w = threadIdx.x >> 6;
         K = s.K;
+        m0w = lds_tile + (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;
         if constexpr (!MN) {
             r0 = make_desc(s.p0, (int64_t)s.rows0 * s.ld * 2);
             r1 = make_desc(s.p1, (int64_t)s.rows1 * s.ld * 2);
@@ -146,6 +163,16 @@ struct DirectLoader {
         }
         const bool hi = !MN && i * NW * RPC_K >= HALF;
         dma_to_lds<16>(hi ? r1 : r0, tile + q * 512, o, so);
+    }
+    // instruction i of K-step kt into the tile at LDS byte address
+    // (stage-0 tile) + stage_off, without the K-tail test: K-step kt must lie
+    // inside K when the rows are K-major (MN-major tiles are masked past K by
+    // the descriptor)
+    __device__ __forceinline__ void issue_fast(uint32_t stage_off, int kt, int i)
+    {
+        const bool hi = !MN && i * NW * RPC_K >= HALF;
+        dma16_to_lds_at(hi ? r1 : r0, m0w + stage_off + (uint32_t)(i * NW * 1024), off[i],
+                        (uint32_t)kt * kstep);
     }
     // global -> LDS for K-step kt into the tile at `tile` (TILE_BYTES bytes)
     __device__ __forceinline__ void issue(uint16_t* tile, int kt)
