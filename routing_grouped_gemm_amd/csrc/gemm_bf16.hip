@@ -28,9 +28,10 @@
 
 #include "gemm_common.h"
 
-// MFMAs issued per direct-load instruction of the next K-step
-#ifndef MOE_GEMM_LOAD_SPREAD
-#define MOE_GEMM_LOAD_SPREAD 2
+// the direct loads of the next K-step go out spread evenly over the first
+// LOAD_SPAN / 32 of a K-step's MFMAs
+#ifndef MOE_GEMM_LOAD_SPAN
+#define MOE_GEMM_LOAD_SPAN 12
 #endif
 
 namespace moe {
@@ -91,11 +92,12 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
     using LB = DirectLoader<BN, BK, B_MN, NW>;
     constexpr int NA = LA::PER_WAVE;
     constexpr int NB = LB::PER_WAVE;
-    constexpr int SPREAD = MOE_GEMM_LOAD_SPREAD;   // MFMAs per load instruction
-    constexpr int QPS = MI * NJ / SPREAD;          // load instructions per k-slice of MFMAs
+    constexpr int NQ = NA + NB;                    // load instructions per wave per K-step
+    constexpr int SM = MI * NJ;                    // MFMAs per k-slice
+    constexpr int SPAN = MOE_GEMM_LOAD_SPAN * KS * SM / 32 < NQ ? NQ : MOE_GEMM_LOAD_SPAN * KS * SM / 32;
     static_assert(NS == 2, "two LDS stages");
     static_assert(KS >= 2 && KS % 2 == 0, "an even number of k-slices per K-step");
-    static_assert(NA + NB <= 2 * QPS, "the loads fit the MFMAs of two k-slices");
+    static_assert(SPAN <= KS * SM, "the loads fit the K-step's MFMAs");
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -125,20 +127,24 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
 #pragma unroll
         for (int j = 0; j < NJ; ++j) bfr[buf][j] = read_frag<BN, BK, B_MN>(b_s, WL<NW>::sub_col(wn, j), ks, lane);
     };
-    // the MFMAs of one k-slice from fragment buffer buf; load instruction
-    // q0 + m / SPREAD goes out after the m-th MFMA when m % SPREAD == SPREAD-1
-    auto slice = [&](int buf, int q0, auto&& load) __attribute__((always_inline)) {
+    // the MFMAs of one k-slice from fragment buffer buf; m0: index of its
+    // first MFMA in the K-step's sequence (the previous K-step's last slice,
+    // then slices 0 .. KS-2); load instruction q goes out after MFMA
+    // (q + 1) * SPAN / NQ - 1
+    auto slice = [&](int buf, int m0, auto&& load) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][j], af[buf][i], acc[i][j], 0, 0, 0);
-                const int m = i * NJ + j;
-                if (m % SPREAD == SPREAD - 1 && q0 + m / SPREAD < NA + NB) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    load(q0 + m / SPREAD);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                const int m = m0 + i * NJ + j;
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    if ((q + 1) * SPAN / NQ - 1 == m) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        load(q);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
             }
     };
 
@@ -168,14 +174,15 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
             slice(1, 0, load);   // the last k-slice of K-step kt-1
         } else {
 #pragma unroll
-            for (int q = 0; q < QPS && q < NA + NB; ++q) load(q);
+            for (int q = 0; q < NQ; ++q)
+                if ((q + 1) * SPAN / NQ - 1 < SM) load(q);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks + 1 < KS; ++ks) {
             read((ks + 1) & 1, a_s, b_s, ks + 1);
             __builtin_amdgcn_sched_barrier(0);
-            slice(ks & 1, (ks + 1) * QPS, load);
+            slice(ks & 1, (ks + 1) * SM, load);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -187,7 +194,7 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
     } else {
         for (int kt = 0; kt < nk; ++kt) kstep(kt, std::integral_constant<int, 2>{});
     }
-    slice(1, NA + NB, [](int) __attribute__((always_inline)) {});   // the last k-slice of the last K-step
+    slice(1, KS * SM, [](int) __attribute__((always_inline)) {});   // the last k-slice of the last K-step
     __syncthreads();  // the LDS may be reused by the caller
 }
 

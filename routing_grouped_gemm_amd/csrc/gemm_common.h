@@ -123,8 +123,8 @@ struct DirectLoader {
         K = s.K;
         m0w = lds_tile + (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;
         if constexpr (!MN) {
-            r0 = make_desc(s.p0, (int64_t)s.rows0 * s.ld * 2);
-            r1 = make_desc(s.p1, (int64_t)s.rows1 * s.ld * 2);
+            r0 = wave_uniform(make_desc(s.p0, (int64_t)s.rows0 * s.ld * 2));
+            r1 = wave_uniform(make_desc(s.p1, (int64_t)s.rows1 * s.ld * 2));
             kstep = BK * 2;
 #pragma unroll
             for (int i = 0; i < PER_WAVE; ++i) {
@@ -135,7 +135,7 @@ struct DirectLoader {
                 off[i] = (uint32_t)(rr * s.ld * 2 + c * 16);
             }
         } else {
-            r0 = r1 = make_desc(s.p0, (int64_t)s.K * s.ld * 2);
+            r0 = r1 = wave_uniform(make_desc(s.p0, (int64_t)s.K * s.ld * 2));
             kstep = (uint32_t)(BK * s.ld * 2);
             constexpr int KROWS = 1024 / (ROWS * 2);   // k-rows per 1 KB chunk
             constexpr int CPR = ROWS / 8;              // 16-byte chunks per k-row
