@@ -30,6 +30,11 @@
 
 // the direct loads of the next K-step go out spread evenly over the first
 // LOAD_SPAN / 32 of a K-step's MFMAs
+// ping-pong main loop for the grouped-M GEMMs with K-major weights (K a
+// multiple of 64); measured slower than the default loop with MN-major ones
+#ifndef MOE_GEMM_PINGPONG
+#define MOE_GEMM_PINGPONG 1
+#endif
 #ifndef MOE_GEMM_LOAD_SPAN
 #define MOE_GEMM_LOAD_SPAN 12
 #endif
@@ -198,6 +203,182 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
     __syncthreads();  // the LDS may be reused by the caller
 }
 
+// Direct loads of half of a K-major 256 x 64 tile (the layout DirectLoader
+// writes): 1 KB chunks half*16 + 4i + w4, i = 0..3, of the 32 chunks of a
+// K-step; half 0 is rows 0..127, half 1 rows 128..255.
+template <int ROWS, int BK>
+struct HalfLoader {
+    static_assert(ROWS == 256 && BK == 64, "256 x 64 tiles");
+    static constexpr int CPR_K = BK / 8;          // 16-byte chunks per row
+    static constexpr int RPC_K = 1024 / (BK * 2); // rows per 1 KB chunk
+    desc_t d;
+    uint32_t off[4];
+    uint32_t m0w;     // LDS byte address of chunk half*16 + w4 of the stage-0 tile
+    __device__ __forceinline__ void init(const TileSrc& s, uint32_t lds_tile, int half, int w4)
+    {
+        const int lane = threadIdx.x & 63;
+        m0w = lds_tile + (uint32_t)(half * 16 + w4) * 1024u;
+        d = wave_uniform(half ? make_desc(s.p1, (int64_t)s.rows1 * s.ld * 2)
+                              : make_desc(s.p0, (int64_t)s.rows0 * s.ld * 2));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = half * 16 + i * 4 + w4;
+            const int row = q * RPC_K + lane / CPR_K;
+            const int c = (int)lds_chunk<false, BK>(row, lane % CPR_K);
+            off[i] = (uint32_t)((row - half * (ROWS / 2)) * s.ld * 2 + c * 16);
+        }
+    }
+    // this wave's 4 chunks of K-step kt into the stage at byte offset stage_off
+    __device__ __forceinline__ void issue(uint32_t stage_off, int kt)
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dma16_to_lds_at(d, m0w + stage_off + (uint32_t)i * 4096u, off[i], (uint32_t)(kt * BK * 2));
+    }
+};
+
+// Ping-pong main loop of a 256 x 256 tile, 8 waves, K-major operands, K a
+// multiple of 64.
+// The two waves of a SIMD belong to different groups (waves 0..3: tile rows
+// 0..127, waves 4..7: rows 128..255) that alternate, tick by tick, between
+// issuing the 16 MFMAs of one half K-step (32 k) from registers and reading
+// the fragments of their next half K-step from LDS; a barrier ends every
+// tick.  Group 1 runs one tick behind group 0, so every tick one wave per
+// SIMD keeps the MFMA pipe busy while the other one does memory work.
+// Each quarter of a K-step's operands (A rows 0..127, B chunks 0..15,
+// B chunks 16..31, A rows 128..255) is loaded into its LDS stage by the
+// group in memory phase as soon as the K-step two back has finished reading
+// that quarter: 4 direct loads per wave per memory tick, 3 to 5 ticks before
+// the data is read.
+template <bool B_MN>
+__device__ __forceinline__ void mainloop_pp(const TileSrc& sa, const TileSrc& sb, f32x16 (&acc)[4][2],
+                                            uint16_t* smem)
+{
+    constexpr int BM = 256, BK = 64, MI = 4, NJ = 2;
+    constexpr int STAGE = (BM + BN) * BK;   // elements per stage
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = wave >> 2;    // group
+    const int w4 = wave & 3;    // wave column (and SIMD)
+
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nk = sa.K / BK;
+    if (nk == 0) return;
+    const int H = 2 * nk;   // half K-steps
+    // K-steps 0 and 1, whole tiles
+    {
+        DirectLoader<BM, BK, false, 8> la;
+        DirectLoader<BN, BK, B_MN, 8> lb;
+        la.init(sa);
+        lb.init(sb);
+        la.issue(smem, 0);
+        lb.issue(smem + BM * BK, 0);
+        if (nk > 1) {
+            la.issue(smem + STAGE, 1);
+            lb.issue(smem + STAGE + BM * BK, 1);
+        }
+    }
+    // later K-steps: group 0 loads B half 0 and A half 1, group 1 A half 0 and B half 1
+    static_assert(!B_MN, "K-major weights");
+    HalfLoader<BM, BK> ha;
+    HalfLoader<BN, BK> hb;
+    ha.init(sa, lds_addr(smem), g == 0 ? 1 : 0, w4);
+    hb.init(sb, lds_addr(smem + BM * BK), g, w4);
+    if (nk > 1) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+
+    bf16x8 af[2][MI], bfr[2][NJ];
+    auto read_hs = [&](int hs) __attribute__((always_inline)) {
+        const uint16_t* a_s = smem + ((hs >> 1) & 1) * STAGE;
+        const uint16_t* b_s = a_s + BM * BK;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int ks = (hs & 1) * 2 + s;
+#pragma unroll
+            for (int i = 0; i < MI; ++i) af[s][i] = read_frag<BM, BK, false>(a_s, g * 128 + i * 32, ks, lane);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) bfr[s][j] = read_frag<BN, BK, B_MN>(b_s, WL<8>::sub_col(w4, j), ks, lane);
+        }
+    };
+    auto compute = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s][j], af[s][i], acc[i][j], 0, 0, 0);
+    };
+    // direct loads of this wave's memory tick t
+    auto loads = [&](int t) __attribute__((always_inline)) {
+        int j;
+        if (g == 0) {
+            if ((t & 3) == 3) {          // B half 0 of K-step j
+                j = (t + 5) >> 2;
+                if (j >= 2 && j < nk) hb.issue((uint32_t)(j & 1) * STAGE * 2, j);
+            } else {                     // t % 4 == 1: A half 1 (rows 128..255)
+                j = (t + 3) >> 2;
+                if (j >= 2 && j < nk) ha.issue((uint32_t)(j & 1) * STAGE * 2, j);
+            }
+        } else {
+            if ((t & 3) == 2) {          // A half 0 (rows 0..127)
+                j = (t + 6) >> 2;
+                if (j >= 2 && j < nk) ha.issue((uint32_t)(j & 1) * STAGE * 2, j);
+            } else {                     // t % 4 == 0: B half 1
+                j = (t >> 2) + 1;
+                if (j >= 2 && j < nk) hb.issue((uint32_t)(j & 1) * STAGE * 2, j);
+            }
+        }
+    };
+    // end of tick t: the loads the next ticks read have landed, then the barrier
+    auto end_tick = [&](int t) __attribute__((always_inline)) {
+        if ((t & 3) == 2) {
+            // group 0 needs its B half 0 of K-step (t+2)/4 (its A half 1 of that
+            // K-step, issued a tick later, may stay in flight); group 1 its A
+            // half 0 and B half 1 of that K-step (its A half 0 of the next
+            // one, issued this tick, may stay in flight)
+            const int j = g == 0 ? (t + 2) >> 2 : (t + 6) >> 2;
+            if (j >= 2 && j < nk) wait_vmcnt<4>();
+            else wait_vmcnt<0>();
+        } else if ((t & 3) == 3 && g == 0) {
+            // group 0 needs its A half 1 of K-step (t+1)/4 (B half 0 of the
+            // next one, issued this tick, may stay in flight)
+            const int j = (t + 5) >> 2;
+            if (j >= 2 && j < nk) wait_vmcnt<4>();
+            else wait_vmcnt<0>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    if (g == 0) {
+        read_hs(0);
+        for (int u = 0; u < H; ++u) {
+            compute();                       // tick 2u
+            end_tick(2 * u);
+            loads(2 * u + 1);                // tick 2u+1
+            if (u + 1 < H) read_hs(u + 1);
+            end_tick(2 * u + 1);
+        }
+    } else {
+        for (int u = 0; u < H; ++u) {
+            loads(2 * u);                    // tick 2u
+            read_hs(u);
+            end_tick(2 * u);
+            compute();                       // tick 2u+1
+            end_tick(2 * u + 1);
+        }
+    }
+}
+
 // Grouped-M GEMM: C[rows of group e] = A[rows of group e] x B_e^T (B_MN = false:
 // B_e stored [N, K]) or A x B_e (B_MN = true: B_e stored [K, N]).
 template <int BM, int BK, int NS, bool B_MN, int EPI, int NW, bool KAL>
@@ -245,7 +426,10 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_m_kernel(MParams p)
     }
 
     f32x16 acc[BM / 64][WL<NW>::NJ];
-    mainloop<BM, BK, NS, false, B_MN, NW, KAL>(sa, sb, acc, smem);
+    if constexpr (KAL && !B_MN && NW == 8 && BM == 256 && BK == 64 && MOE_GEMM_PINGPONG)
+        mainloop_pp<B_MN>(sa, sb, acc, smem);
+    else
+        mainloop<BM, BK, NS, false, B_MN, NW, KAL>(sa, sb, acc, smem);
     epilogue_m<BM, EPI, NW>(acc, p, row0, rows_valid, nt, reinterpret_cast<uint8_t*>(smem));
 }
 
