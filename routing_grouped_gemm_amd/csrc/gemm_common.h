@@ -5,6 +5,7 @@
 
 #include "moe_internal.h"
 
+
 namespace moe {
 namespace gemm {
 
@@ -274,6 +275,15 @@ __device__ __forceinline__ uint32_t stage_off(int r, int col)   // element (r, c
     return (uint32_t)(r * (CH * 16) + (((col >> 3) ^ (r & (CH - 1))) << 4) + ((col & 4) << 1));
 }
 
+// 16-byte non-temporal (streaming) store, for outputs that nothing reads
+// back while they could still be in L2 (the weight gradients: measured 6%
+// faster than plain stores there, no change for the forward / dgrad outputs)
+__device__ __forceinline__ void store16(uint16_t* p, uint4 v)
+{
+    typedef __attribute__((ext_vector_type(4))) uint32_t vu4;
+    __builtin_nontemporal_store(vu4{v.x, v.y, v.z, v.w}, reinterpret_cast<vu4*>(p));
+}
+
 __device__ __forceinline__ void stage_put(uint8_t* lds, uint32_t off, uint2 v)
 {
     *reinterpret_cast<uint2*>(lds + off) = v;
@@ -481,7 +491,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[BM / 64][WL<NW>::
     stage_acc<BM, NW>(acc, lds);
     stage_flush<BM, 32, WL<NW>::NT>(lds, [&](int r, int c, uint4 v) {
         const int n = col0 + 8 * c;
-        if (r < rows && n < N) *reinterpret_cast<uint4*>(C + r * ldc + n) = v;
+        if (r < rows && n < N) store16(C + r * ldc + n, v);
     });
 }
 
