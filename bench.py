@@ -33,11 +33,11 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 STAGES = ["route", "permute", "gemm_gate_up", "gemm_down", "combine", "combine_bwd",
           "gemm_dgrad_down", "gemm_dgrad_gate_up", "gemm_wgrad", "permute_bwd"]
 KERNEL_NAMES = {
-    "gemm_gate_up": "gemm_grouped_m_kernel<256, 64, 2, false, 1> (gate/up + SwiGLU)",
-    "gemm_down": "gemm_grouped_m_kernel<256, 64, 2, false, 0> (down)",
-    "gemm_dgrad_down": "gemm_grouped_m_kernel<256, 64, 2, true, 2> (dgrad down + SwiGLU bwd)",
-    "gemm_dgrad_gate_up": "gemm_grouped_m_kernel<256, 64, 2, true, 0> (dgrad gate/up)",
-    "gemm_wgrad": "gemm_grouped_k_kernel<256, 64, 2> (wgrad, dWd and dW13 in one launch)",
+    "gemm_gate_up": "gemm_grouped_m_kernel<256, 64, 2, false, 1, 8, true> (gate/up + SwiGLU)",
+    "gemm_down": "gemm_grouped_m_kernel<256, 64, 2, false, 0, 8, true> (down)",
+    "gemm_dgrad_down": "gemm_grouped_m_kernel<256, 64, 2, true, 2, 8, true> (dgrad down + SwiGLU bwd)",
+    "gemm_dgrad_gate_up": "gemm_grouped_m_kernel<256, 64, 2, true, 0, 8, true> (dgrad gate/up)",
+    "gemm_wgrad": "gemm_grouped_k_kernel<256, 64, 2, 8> (wgrad, dWd and dW13 in one launch)",
     "permute": "permute_kernel<true, false, {k}>",
     "combine": "combine_kernel<true, {k}>",
     "combine_bwd": "permute_kernel<true, true, {k}>",
