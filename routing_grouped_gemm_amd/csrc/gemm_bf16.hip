@@ -11,18 +11,20 @@
 //     adjacent, and workgroup ids are remapped so that a contiguous range of
 //     tiles lands on one XCD (consecutive ids go round-robin over the 8 XCDs):
 //     the M-tiles sharing a weight tile then share that XCD's L2;
-//   - tiles are BM x 256 x 64, four waves in a 2 x 2 grid, each wave owning
-//     (BM/2) x 128 of fp32 accumulators; operands are staged in LDS (row pitch
-//     144 B: conflict-free 16-byte fragment reads), double-buffered so the
-//     next K-step's global loads are in flight during the MFMAs;
-//   - operands stored with K contiguous are copied to LDS as 16-byte
-//     vectors; operands stored with M/N contiguous (the weight in dgrad, both
-//     operands of wgrad) are read as 8 k-rows x 16 bytes per thread and
-//     transposed in registers before the 16-byte LDS stores;
-//   - epilogues: plain bf16 store; the SwiGLU forward (each wave holds the
-//     gate and up accumulators of the same columns, so h = silu(g) * u is
-//     formed in registers and g, u, h are stored); the SwiGLU backward (reads
-//     the saved g, u of its elements and stores dg, du).
+//   - tiles are 256 x 256 x 64, eight waves (two per SIMD) in a 2 x 4 grid,
+//     each wave owning 128 x 64 fp32 accumulators; operands go from HBM to
+//     LDS with direct loads (no VGPR staging) into two XOR-swizzled stages;
+//   - operands stored with M/N contiguous (the weight in dgrad, both operands
+//     of wgrad) are read from LDS with the gfx950 transposing reads;
+//   - two main loops: the default one (fragment reads one k-slice ahead, the
+//     last slice's MFMAs after the next barrier, the next K-step's loads
+//     spread over the first MFMAs) and a ping-pong one for K-major weights
+//     (the two waves of a SIMD alternate between MFMA-only and memory ticks);
+//   - epilogues, staged through LDS so that each lane stores 16 contiguous
+//     bytes: plain bf16 store; the SwiGLU forward (each wave holds the gate
+//     and up accumulators of the same columns, so h = silu(g) * u is formed
+//     in registers and g, u, h are stored); the SwiGLU backward (reads the
+//     saved g, u of its elements and stores dg, du).
 // Accumulation is fp32; bf16 results are rounded to nearest even.
 #include <type_traits>
 
