@@ -37,6 +37,11 @@
 #ifndef MOE_GEMM_PINGPONG
 #define MOE_GEMM_PINGPONG 1
 #endif
+// 64- or 128-row tiles for the last M-tile of an expert when it has at most
+// 64 or 128 rows
+#ifndef MOE_GEMM_SMALL_TAIL
+#define MOE_GEMM_SMALL_TAIL 1
+#endif
 #ifndef MOE_GEMM_LOAD_SPAN
 #define MOE_GEMM_LOAD_SPAN 12
 #endif
@@ -427,6 +432,29 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_m_kernel(MParams p)
         sb.rows1 = max(min(128, p.N - n0 - 128), 0);
     }
 
+    if constexpr (BM == 256 && MOE_GEMM_SMALL_TAIL) {
+        // the last M-tile of an expert with at most 64 (128) rows: a 64-row
+        // (128-row) tile, with a quarter (half) of the MFMAs and of the A
+        // loads of a full tile
+        auto small = [&](auto BMS_) __attribute__((always_inline)) {
+            constexpr int BMS = decltype(BMS_)::value;
+            TileSrc st = sa;
+            st.p1 = st.p0 + (int64_t)(BMS / 2) * p.lda;
+            st.rows0 = min(rows_valid, BMS / 2);
+            st.rows1 = max(rows_valid - BMS / 2, 0);
+            f32x16 acc_s[BMS / 64][WL<NW>::NJ];
+            mainloop<BMS, BK, NS, false, B_MN, NW, KAL>(st, sb, acc_s, smem);
+            epilogue_m<BMS, EPI, NW>(acc_s, p, row0, rows_valid, nt, reinterpret_cast<uint8_t*>(smem));
+        };
+        if (rows_valid <= 64) {
+            small(std::integral_constant<int, 64>{});
+            return;
+        }
+        if (rows_valid <= 128) {
+            small(std::integral_constant<int, 128>{});
+            return;
+        }
+    }
     f32x16 acc[BM / 64][WL<NW>::NJ];
     if constexpr (KAL && !B_MN && NW == 8 && BM == 256 && BK == 64 && MOE_GEMM_PINGPONG)
         mainloop_pp<B_MN>(sa, sb, acc, smem);

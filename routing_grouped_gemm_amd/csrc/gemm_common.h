@@ -117,6 +117,20 @@ struct DirectLoader {
     uint32_t kstep;           // bytes a K-step advances (scalar)
     uint32_t m0w;             // LDS byte address of this wave's first 1 KB chunk in the stage-0 tile
     int K;
+    // whether instruction i of this wave loads rows of the second half (K-major):
+    // a function of i alone when every chunk row-block of one i lies in one
+    // half for all waves, else of i and the (wave-uniform) wave index
+    __device__ __forceinline__ bool half_of(int i) const
+    {
+        if constexpr (MN) {
+            return false;
+        } else if constexpr (HALF % (NW * RPC_K) == 0) {
+            return i * NW * RPC_K >= HALF;
+        } else {
+            const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+            return (i * NW + w) * RPC_K >= HALF;
+        }
+    }
     __device__ __forceinline__ void init(const TileSrc& s, uint32_t lds_tile = 0)
     {
         const int lane = threadIdx.x & 63;
@@ -162,7 +176,7 @@ struct DirectLoader {
             const int c = (int)lds_chunk<false, BK>(row, lane % CPR_K);
             if (kt * BK + c * 8 >= K) o = kOOB;
         }
-        const bool hi = !MN && i * NW * RPC_K >= HALF;
+        const bool hi = half_of(i);
         dma_to_lds<16>(hi ? r1 : r0, tile + q * 512, o, so);
     }
     // instruction i of K-step kt into the tile at LDS byte address
@@ -171,7 +185,7 @@ struct DirectLoader {
     // the descriptor)
     __device__ __forceinline__ void issue_fast(uint32_t stage_off, int kt, int i)
     {
-        const bool hi = !MN && i * NW * RPC_K >= HALF;
+        const bool hi = half_of(i);
         dma16_to_lds_at(hi ? r1 : r0, m0w + stage_off + (uint32_t)(i * NW * 1024), off[i],
                         (uint32_t)kt * kstep);
     }

@@ -119,6 +119,11 @@ LAYER_CASES = [
     (400, 128, 8, 128, 2, "bf16", 70),
     (256, 128, 8, 256, 2, "f32", 0),
     (130, 72, 3, 40, 2, "f32", 0),
+    # last M-tiles of at most 64 / 128 rows (the 64- and 128-row tile paths):
+    # about 275, 53 and 350 rows per expert
+    (1100, 256, 4, 256, 1, "bf16", 0),
+    (160, 128, 6, 128, 2, "bf16", 0),
+    (1400, 256, 4, 256, 1, "bf16", 0),
 ]
 
 
