@@ -89,6 +89,47 @@ __global__ __launch_bounds__(256) void zero_rows_kernel(const int32_t* __restric
     }
 }
 
+// One 32-element block: the scale exponent and the 32 E4M3FN codes (four per
+// word, element 4*wi + b in byte b of w[wi]).  When every element is finite
+// the scaled values lie within +-448 and the hardware packed conversion
+// (round to nearest even) gives the codes; it was checked to agree with
+// f32_to_e4m3 on every finite input of magnitude <= 448 tried: each E4M3
+// value, each midpoint between neighbours and their fp32 neighbours, and
+// four million random values over the range and over scales 2^-20 .. 2^9.
+// Blocks with a NaN or an infinity take f32_to_e4m3 (saturation and NaN rules
+// of the format).
+__device__ __forceinline__ int quant_block32(const float (&vals)[32], uint32_t (&w)[8])
+{
+    float amax = 0.0f;
+    bool finite = true;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const float a = fabsf(vals[i]);
+        amax = fmaxf(amax, a);
+        finite &= a <= 3.402823466e38f;   // false for NaN and infinities
+    }
+    const int e = mx_scale_exp(amax);
+    if (finite) {
+#pragma unroll
+        for (int wi = 0; wi < 8; ++wi) {
+            // ldexp keeps the exact product even when 2^-e overflows fp32 (e = -127)
+            const float q0 = __builtin_ldexpf(vals[wi * 4 + 0], -e), q1 = __builtin_ldexpf(vals[wi * 4 + 1], -e);
+            const float q2 = __builtin_ldexpf(vals[wi * 4 + 2], -e), q3 = __builtin_ldexpf(vals[wi * 4 + 3], -e);
+            const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+            w[wi] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, lo, true);
+        }
+    } else {
+#pragma unroll
+        for (int wi = 0; wi < 8; ++wi) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) word |= f32_to_e4m3(__builtin_ldexpf(vals[wi * 4 + b], -e)) << (8 * b);
+            w[wi] = word;
+        }
+    }
+    return e;
+}
+
 // quantise 32 bf16 (four 16-byte vectors) into 32 E4M3FN codes + scale exponent
 __device__ __forceinline__ int quant32(const uint4 (&in)[4], uint4 (&out)[2])
 {
@@ -102,22 +143,8 @@ __device__ __forceinline__ int quant32(const uint4 (&in)[4], uint4 (&out)[2])
             vals[q * 8 + 2 * p + 1] = bf16_hi(w[p]);
         }
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(vals[i]));
-    const int e = mx_scale_exp(amax);
     uint32_t c[8];
-#pragma unroll
-    for (int wi = 0; wi < 8; ++wi) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            // ldexp keeps the exact product even when 2^-e overflows fp32 (e = -127)
-            const float q = __builtin_ldexpf(vals[wi * 4 + b], -e);
-            word |= f32_to_e4m3(q) << (8 * b);
-        }
-        c[wi] = word;
-    }
+    const int e = quant_block32(vals, c);
     out[0] = make_uint4(c[0], c[1], c[2], c[3]);
     out[1] = make_uint4(c[4], c[5], c[6], c[7]);
     return e;
@@ -177,10 +204,12 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint4* __restrict
 // Column-wise quantiser inside row groups.  Each group's rows are padded to a
 // multiple of kMxColPad (zero codes) and stored transposed, so that a GEMM
 // over the group reads whole 128-element K-steps and 4-byte scale words.
-// Block (cb, L): columns [cb*256, cb*256+256) of the L-th 32-row block in the
-// concatenation of all groups' padded row blocks (device schedule from the
-// group offsets).  Each thread quantises one column over those 32 rows and
-// writes the 32 codes as one 32-byte run of the transposed group layout.
+// Block (cb, L): columns [cb*128, cb*128+128) of the L-th 128-row tile in the
+// concatenation of all groups' padded rows (device schedule from the group
+// offsets).  The tile comes into LDS with coalesced row loads; each thread
+// then quantises one column over two of the tile's four 32-row blocks, and
+// the codes leave as whole 128-byte runs of the transposed layout (one
+// column's 128 rows), eight lanes per run.
 template <bool FROM_MX>
 __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restrict__ src,
                                                          const uint8_t* __restrict__ src_codes,
@@ -191,59 +220,117 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
                                                          uint8_t* __restrict__ codes,
                                                          uint8_t* __restrict__ scales)
 {
+    constexpr int TR = kMxColPad;   // 128 rows per tile
+    constexpr int TC = 128;         // columns per tile
+    constexpr int EB = FROM_MX ? 1 : 2;   // input bytes per element
     __shared__ int s_pref[kMaxExperts + 1];
     __shared__ int s_part[256];
-    constexpr int BPP = kMxColPad / 32;   // 32-row blocks per padding unit
-    int g = 0, rb = blockIdx.y;
+    // the input tile (row-major); after the quantisation the codes reuse it
+    // as [block b][column c][32 rows]
+    static_assert(TR * TC * EB >= 4 * TC * 32, "codes fit the input tile");
+    __shared__ __align__(16) uint8_t s_in[TR * TC * EB];
+    __shared__ uint32_t s_rsc[FROM_MX ? TR : 1];            // FROM_MX: each row's 4 scale bytes
+    __shared__ uint8_t s_osc[TC * 4];                       // scales as [column c][block b]
+    uint8_t* s_out = s_in;
+    int g = 0, rt = blockIdx.y;
     int64_t g0 = 0, g1 = rows, P = 0;
     if (group_off || capacity > 0) {
-        const int total = block_tile_prefix<256>(group_off, capacity, n_groups, rows, kMxColPad,
-                                                 BPP, s_pref, s_part);
+        const int total = block_tile_prefix<256>(group_off, capacity, n_groups, rows, TR, 1, s_pref, s_part);
         if ((int)blockIdx.y >= total) return;
         g = find_group(s_pref, n_groups, blockIdx.y);
-        rb = blockIdx.y - s_pref[g];
+        rt = blockIdx.y - s_pref[g];
         g0 = group_begin(group_off, capacity, g, rows);
         g1 = g0 + group_rows(group_off, capacity, g, rows);
-        P = (int64_t)s_pref[g] * 32;              // padded rows of earlier groups
-    } else if ((int64_t)rb * 32 >= (rows + kMxColPad - 1) / kMxColPad * kMxColPad) {
+        P = (int64_t)s_pref[g] * TR;              // padded rows of earlier groups
+    } else if ((int64_t)rt * TR >= rows) {
         return;
     }
-    const int c = blockIdx.x * 256 + threadIdx.x;
-    if (c >= K) return;
-    const int64_t mpad = (g1 - g0 + kMxColPad - 1) / kMxColPad * kMxColPad;
-    float vals[32];
-    float amax = 0.0f;
+    const int64_t mpad = (g1 - g0 + TR - 1) / TR * TR;
+    const int c0 = blockIdx.x * TC;
+    const int64_t r0 = g0 + (int64_t)rt * TR;
+    const int tid = threadIdx.x;
+
+    // the input tile: TR rows x TC columns (rows past the group and columns
+    // past K read as zero), 16 bytes per lane per load
+    constexpr int CPR = TC * EB / 16;             // 16-byte chunks per tile row
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-        const int64_t row = g0 + (int64_t)rb * 32 + r;
-        float v = 0.0f;
-        if (row < g1) {
-            if constexpr (FROM_MX) {
-                const uint32_t code = src_codes[row * K + c];
-                const int se = (int)src_scales[row * (K / 32) + c / 32] - 127;
-                const int ex = (code >> 3) & 0xF, mt = code & 7;
-                const float a = ex == 0 ? (float)mt * 0.001953125f : __builtin_ldexpf(8.0f + mt, ex - 10);
-                v = __builtin_ldexpf((code & 0x80) ? -a : a, se);
-            } else {
-                v = bf16_to_f32(src[row * K + c]);
-            }
+    for (int q = tid; q < TR * CPR; q += 256) {
+        const int r = q / CPR, cc = q % CPR;
+        const int64_t row = r0 + r;
+        const int col = c0 + cc * (16 / EB);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (row < g1 && col < K) {
+            if constexpr (FROM_MX)
+                v = *reinterpret_cast<const uint4*>(src_codes + row * K + col);
+            else
+                v = *reinterpret_cast<const uint4*>(src + row * K + col);
         }
-        vals[r] = v;
-        amax = fmaxf(amax, fabsf(v));
+        *reinterpret_cast<uint4*>(s_in + r * (TC * EB) + cc * 16) = v;
     }
-    const int e = mx_scale_exp(amax);
-    uint32_t w[8];
+    if constexpr (FROM_MX) {
+        if (tid < TR) {
+            const int64_t row = r0 + tid;
+            uint32_t w = 0;
+            if (row < g1) {
 #pragma unroll
-    for (int wi = 0; wi < 8; ++wi) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) word |= f32_to_e4m3(__builtin_ldexpf(vals[wi * 4 + b], -e)) << (8 * b);
-        w[wi] = word;
+                for (int b = 0; b < TC / 32; ++b) {
+                    const int cb = c0 / 32 + b;
+                    if (cb < K / 32) w |= (uint32_t)src_scales[row * (K / 32) + cb] << (8 * b);
+                }
+            }
+            s_rsc[tid] = w;
+        }
     }
-    uint4* dst = reinterpret_cast<uint4*>(codes + (int64_t)K * P + (int64_t)c * mpad + rb * 32);
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    scales[(int64_t)K * P / 32 + (int64_t)c * (mpad / 32) + rb] = (uint8_t)(e + 127);
+    __syncthreads();
+
+    // one column, 32-row blocks b and b + 2
+    const int c = tid % TC;
+    uint4 cw[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int b = tid / TC + 2 * h;
+        float vals[32];
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            const int rr = b * 32 + r;
+            float v;
+            if constexpr (FROM_MX) {
+                // E4M3FN decode (exact; 0x7F / 0xFF are NaN) times the row's block scale
+                const int code = s_in[rr * TC + c];
+                const int se = (int)((s_rsc[rr] >> (8 * (c / 32))) & 0xffu) - 127;
+                v = __builtin_ldexpf(__builtin_amdgcn_cvt_f32_fp8(code, 0), se);
+            } else {
+                v = bf16_to_f32(*reinterpret_cast<const uint16_t*>(s_in + rr * (TC * 2) + c * 2));
+            }
+            vals[r] = v;
+        }
+        uint32_t w[8];
+        const int e = quant_block32(vals, w);
+        cw[h][0] = make_uint4(w[0], w[1], w[2], w[3]);
+        cw[h][1] = make_uint4(w[4], w[5], w[6], w[7]);
+        s_osc[c * 4 + b] = (uint8_t)(e + 127);
+    }
+    __syncthreads();   // every thread has read its columns: the tile's LDS takes the codes
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint4* o = reinterpret_cast<uint4*>(s_out + ((tid / TC + 2 * h) * TC + c) * 32);
+        o[0] = cw[h][0];
+        o[1] = cw[h][1];
+    }
+    __syncthreads();
+
+    // codes: column c's 128 rows are one 128-byte run of the group layout
+    uint8_t* gcodes = codes + (int64_t)K * P + rt * TR;
+#pragma unroll
+    for (int q = tid; q < TC * 8; q += 256) {
+        const int cc = q / 8, hh = q % 8;          // column, 16-byte piece of its run
+        if (c0 + cc < K)
+            *reinterpret_cast<uint4*>(gcodes + (int64_t)(c0 + cc) * mpad + hh * 16) =
+                *reinterpret_cast<const uint4*>(s_out + ((hh / 2) * TC + cc) * 32 + (hh % 2) * 16);
+    }
+    if (tid < TC && c0 + tid < K)
+        *reinterpret_cast<uint32_t*>(scales + (int64_t)K * P / 32 + (int64_t)(c0 + tid) * (mpad / 32) + rt * 4) =
+            *reinterpret_cast<const uint32_t*>(s_osc + tid * 4);
 }
 
 // thread i makes vector (i % nvec) of token (i / nvec): the K destination
@@ -413,11 +500,11 @@ static hipError_t launch_cols(bool from_mx, const uint16_t* src, const uint8_t* 
                               int capacity, int n_groups, uint8_t* codes, uint8_t* scales,
                               hipStream_t s)
 {
-    // bound on the number of 32-row blocks over all padded groups
+    // bound on the number of 128-row tiles over all padded groups
     const int64_t ngr = group_off || capacity > 0 ? n_groups : 1;
-    const int64_t nrb = (rows + ngr * kMxColPad) / 32;
-    if (nrb == 0 || K == 0) return hipGetLastError();
-    const dim3 grid((unsigned)((K + 255) / 256), (unsigned)nrb);
+    const int64_t nrt = (rows + ngr * kMxColPad) / kMxColPad;
+    if (nrt == 0 || K == 0) return hipGetLastError();
+    const dim3 grid((unsigned)((K + 127) / 128), (unsigned)nrt);
     if (from_mx)
         hipLaunchKernelGGL((quant_cols_kernel<true>), grid, dim3(256), 0, s, src, sc, ss, rows, K,
                            group_off, capacity, n_groups, codes, scales);
