@@ -253,19 +253,26 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
     // the input tile: TR rows x TC columns (rows past the group and columns
     // past K read as zero), 16 bytes per lane per load
     constexpr int CPR = TC * EB / 16;             // 16-byte chunks per tile row
+    constexpr int NLD = TR * CPR / 256;           // loads per thread, all in flight together
+    uint4 ld[NLD];
 #pragma unroll
-    for (int q = tid; q < TR * CPR; q += 256) {
+    for (int i = 0; i < NLD; ++i) {
+        const int q = tid + i * 256;
         const int r = q / CPR, cc = q % CPR;
         const int64_t row = r0 + r;
         const int col = c0 + cc * (16 / EB);
-        uint4 v = make_uint4(0, 0, 0, 0);
+        ld[i] = make_uint4(0, 0, 0, 0);
         if (row < g1 && col < K) {
             if constexpr (FROM_MX)
-                v = *reinterpret_cast<const uint4*>(src_codes + row * K + col);
+                ld[i] = *reinterpret_cast<const uint4*>(src_codes + row * K + col);
             else
-                v = *reinterpret_cast<const uint4*>(src + row * K + col);
+                ld[i] = *reinterpret_cast<const uint4*>(src + row * K + col);
         }
-        *reinterpret_cast<uint4*>(s_in + r * (TC * EB) + cc * 16) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+        const int q = tid + i * 256;
+        *reinterpret_cast<uint4*>(s_in + (q / CPR) * (TC * EB) + (q % CPR) * 16) = ld[i];
     }
     if constexpr (FROM_MX) {
         if (tid < TR) {
