@@ -49,10 +49,12 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v)
     return sign | ((uint32_t)(ex + 7) << 3) | m3;
 }
 
-// smallest e in [-127, 127] with amax <= 448 * 2^e (amax >= 0, finite)
+// smallest e in [-127, 127] with amax <= 448 * 2^e (amax >= 0); an infinite
+// block maximum takes the largest exponent
 __device__ __forceinline__ int mx_scale_exp(float amax)
 {
     if (!(amax > 0.0f)) return -127;
+    if (!(amax <= 3.402823466e38f)) return 127;
     // amax = m * 2^E, m in [1,2) (subnormal amax handled by frexp)
     int E;
     float m = __builtin_frexpf(amax, &E);              // amax = m * 2^E, m in [0.5, 1)

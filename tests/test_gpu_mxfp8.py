@@ -97,6 +97,41 @@ def test_quantize_cols_bit_exact(moe, sizes, K):
     _check_cols(moe, _bf16((int(go[-1]), K), int(go[-1]) * 3 + K, 0.5), go, K)
 
 
+def _special_bf16(rows, K, seed):
+    """Blocks with NaN, infinities, the largest and smallest bf16 magnitudes,
+    signed zeros and all-zero blocks, among ordinary values."""
+    g = torch.Generator().manual_seed(seed)
+    v = torch.randn(rows, K, generator=g)
+    v[0, 3] = float("nan")
+    v[1, 40] = float("inf")
+    v[2, 70] = float("-inf")
+    v[3, :32] = 0.0
+    v[4, 33:64] = -0.0
+    v[5, 5] = 3.3895e38                       # near the bf16 maximum
+    v[6, 96:128] *= 1e-37                     # tiny block: scale near 2^-127
+    v[7, 0:32] = 2.0 ** -133                  # bf16 subnormals
+    v[8, 64:96] = torch.tensor([448.0 * 2.0 ** -3, 416.0 * 2.0 ** -3, 432.0 * 2.0 ** -3] * 10 + [1.0, -1.0])
+    v[9:11, 10] = float("nan")
+    v[12, :] = float("inf")
+    return v.to(torch.bfloat16)
+
+
+def test_quantize_special_values_bit_exact(moe):
+    _say("quant-special")
+    rows, K = 64, 128
+    x = _special_bf16(rows, K, 5)
+    codes = torch.empty(rows, K, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(rows, K // 32, dtype=torch.uint8, device="cuda")
+    moe.moe_quantize_mxfp8(x.cuda(), 0, codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = oracle.mx_quantize_rows(np64(x))
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    # column-wise over the same values (two groups, the first one ragged)
+    go = np.array([0, 37, rows], np.int32)
+    _check_cols(moe, x, go, K)
+
+
 def test_permute_mx_and_requantise_cols_bit_exact(moe):
     _say("permute-mx")
     T, d, E, k = 700, 256, 6, 2
