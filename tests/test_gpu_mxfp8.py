@@ -186,7 +186,8 @@ def _mx_oracle(inp, k, gate=None):
 
 
 @pytest.mark.parametrize("T,d,E,f,k,empty", [(600, 256, 5, 128, 1, None), (512, 384, 4, 256, 2, None),
-                                              (300, 128, 16, 128, 1, None), (700, 256, 6, 384, 2, 3)])
+                                              (300, 128, 16, 128, 1, None), (700, 256, 6, 384, 2, 3),
+                                              (400, 128, 4, 128, 1, None), (1500, 256, 4, 256, 1, None)])
 def test_mx_layer_fwd_bwd(moe, T, d, E, f, k, empty):
     _say("mx-layer", T, d, E, f, k, "empty expert", empty)
     from routing_grouped_gemm_amd.layer import MoELayer
