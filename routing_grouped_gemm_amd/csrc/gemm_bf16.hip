@@ -30,18 +30,24 @@
 
 #include "gemm_common.h"
 
-// the direct loads of the next K-step go out spread evenly over the first
-// LOAD_SPAN / 32 of a K-step's MFMAs
-// ping-pong main loop for the grouped-M GEMMs with K-major weights (K a
-// multiple of 64); measured slower than the default loop with MN-major ones
+// ping-pong main loop for the grouped-M GEMMs with 256-row tiles and K a
+// multiple of 64 (0: the single-group loop everywhere)
 #ifndef MOE_GEMM_PINGPONG
 #define MOE_GEMM_PINGPONG 1
+#endif
+// the same loop for the weight-gradient GEMM (both operands MN-major, every
+// fragment two transposed LDS reads); measured about 5% slower there than the
+// single-group loop at 256 x 256 tiles over experts of ~512 rows
+#ifndef MOE_GEMM_PINGPONG_K
+#define MOE_GEMM_PINGPONG_K 0
 #endif
 // 64- or 128-row tiles for the last M-tile of an expert when it has at most
 // 64 or 128 rows
 #ifndef MOE_GEMM_SMALL_TAIL
 #define MOE_GEMM_SMALL_TAIL 1
 #endif
+// the direct loads of the next K-step go out spread evenly over the first
+// LOAD_SPAN / 32 of a K-step's MFMAs (single-group loop)
 #ifndef MOE_GEMM_LOAD_SPAN
 #define MOE_GEMM_LOAD_SPAN 12
 #endif
@@ -244,20 +250,100 @@ struct HalfLoader {
     }
 };
 
-// Ping-pong main loop of a 256 x 256 tile, 8 waves, K-major operands, K a
-// multiple of 64.
+// Direct loads of half of an MN-major 64 x 256 tile (k-rows of 256 elements,
+// the layout DirectLoader<256, 64, true> writes): 1 KB chunks (2 k-rows)
+// half*16 + 4i + w4, i = 0..3; half 0 is k-rows 0..31, half 1 k-rows 32..63.
+template <int ROWS, int BK>
+struct HalfLoaderMN {
+    static_assert(ROWS == 256 && BK == 64, "64 x 256 tiles");
+    static constexpr int KROWS = 1024 / (ROWS * 2);   // k-rows per 1 KB chunk
+    static constexpr int CPR = ROWS / 8;              // 16-byte chunks per k-row
+    desc_t d;
+    uint32_t off[4];
+    uint32_t m0w;
+    uint32_t kstep;
+    __device__ __forceinline__ void init(const TileSrc& s, uint32_t lds_tile, int half, int w4)
+    {
+        const int lane = threadIdx.x & 63;
+        m0w = lds_tile + (uint32_t)(half * 16 + w4) * 1024u;
+        d = wave_uniform(make_desc(s.p0, (int64_t)s.K * s.ld * 2));
+        kstep = (uint32_t)(BK * s.ld * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = half * 16 + i * 4 + w4;
+            const int k = q * KROWS + lane / CPR;
+            const int c = (int)lds_chunk<true, BK>(k, lane % CPR);
+            off[i] = c * 8 < s.rows0 ? (uint32_t)(k * s.ld * 2 + c * 16) : kOOB;
+        }
+    }
+    __device__ __forceinline__ void issue(uint32_t stage_off, int kt)
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dma16_to_lds_at(d, m0w + stage_off + (uint32_t)i * 4096u, off[i], (uint32_t)kt * kstep);
+    }
+};
+
+// Direct loads of a column half of an MN-major 64 x 256 tile kept as two
+// 64 x 128 sub-tiles (k-rows of 128 elements, sub-tile h = columns
+// 128h..128h+127 at byte 16384h): 1 KB chunks (4 k-rows) 4i + w4, i = 0..3,
+// of sub-tile `half`.  Chunk placement within a k-row follows lds_chunk<true>.
+template <int BK>
+struct ColHalfLoaderMN {
+    static_assert(BK == 64, "64-deep tiles");
+    static constexpr int CPR = 128 / 8;   // 16-byte chunks per k-row
+    desc_t d;
+    uint32_t off[4];
+    uint32_t m0w;
+    uint32_t kstep;
+    __device__ __forceinline__ void init(const TileSrc& s, uint32_t lds_tile, int half, int w4)
+    {
+        const int lane = threadIdx.x & 63;
+        m0w = lds_tile + (uint32_t)half * 16384u + (uint32_t)w4 * 1024u;
+        d = wave_uniform(make_desc(s.p0, (int64_t)s.K * s.ld * 2));
+        kstep = (uint32_t)(BK * s.ld * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = i * 4 + w4;
+            const int k = q * 4 + lane / CPR;
+            const int col = half * 128 + (int)lds_chunk<true, BK>(k, lane % CPR) * 8;
+            off[i] = col < s.rows0 ? (uint32_t)(k * s.ld * 2 + col * 2) : kOOB;
+        }
+    }
+    __device__ __forceinline__ void issue(uint32_t stage_off, int kt)
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dma16_to_lds_at(d, m0w + stage_off + (uint32_t)i * 4096u, off[i], (uint32_t)kt * kstep);
+    }
+};
+
+// Ping-pong main loop of a 256 x 256 tile, 8 waves, K-major A, K a multiple
+// of 64; B K-major (rows of [N, K] weights) or MN-major ([K, N] weights).
 // The two waves of a SIMD belong to different groups (waves 0..3: tile rows
 // 0..127, waves 4..7: rows 128..255) that alternate, tick by tick, between
-// issuing the 16 MFMAs of one half K-step (32 k) from registers and reading
-// the fragments of their next half K-step from LDS; a barrier ends every
-// tick.  Group 1 runs one tick behind group 0, so every tick one wave per
-// SIMD keeps the MFMA pipe busy while the other one does memory work.
-// Each quarter of a K-step's operands (A rows 0..127, B chunks 0..15,
-// B chunks 16..31, A rows 128..255) is loaded into its LDS stage by the
-// group in memory phase as soon as the K-step two back has finished reading
-// that quarter: 4 direct loads per wave per memory tick, 3 to 5 ticks before
-// the data is read.
-template <bool B_MN>
+// a compute tick and a memory tick, with a barrier at the end of every tick;
+// group 1 runs one tick behind group 0, so on every SIMD one wave keeps the
+// MFMA pipe busy while the other issues loads.
+//  - compute tick: the 16 MFMAs of one half K-step (32 k) from registers,
+//    with the fragments of the group's next half K-step read from LDS in
+//    their shadow (one fragment after each of 12 MFMAs); the first k-slice
+//    of the next half K-step goes into the registers of the first k-slice of
+//    this one once its 8 MFMAs have issued, so three k-slices of fragments
+//    are live instead of four;
+//  - memory tick: this wave's 4 direct loads (4 KB) of one quarter of a
+//    K-step, 16 KB per CU; a direct load blocks the issuing wave for about
+//    as long as the CU's load path takes to accept the CU's 16 of them, so
+//    none go out in compute ticks.
+// The quarters of K-step j (2 LDS stages) go out at ticks 4j-7 (A rows
+// 0..127, group 0), 4j-6 (B half 0, group 1), 4j-5 (B half 1, group 0) and
+// 4j-4 (A rows 128..255, group 1); group 0 reads K-step j at ticks 4j-2 and
+// 4j, group 1 at 4j-1 and 4j+1.  Each quarter is waited for by its loading
+// group at the end of the tick before its first read and is loaded only
+// after the last read of the K-step two back, at an earlier tick.  B halves
+// are rows 0..127 / 128..255 of a K-major tile and k-rows 0..31 / 32..63 of
+// an MN-major one; both groups read all of B.
+template <bool A_MN, bool B_MN>
 __device__ __forceinline__ void mainloop_pp(const TileSrc& sa, const TileSrc& sb, f32x16 (&acc)[4][2],
                                             uint16_t* smem)
 {
@@ -275,114 +361,172 @@ __device__ __forceinline__ void mainloop_pp(const TileSrc& sa, const TileSrc& sb
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int nk = sa.K / BK;
+    // MN-major operands: the rows past K (K = the group's rows) read as zeros
+    const int nk = A_MN ? (sa.K + BK - 1) / BK : sa.K / BK;
     if (nk == 0) return;
     const int H = 2 * nk;   // half K-steps
-    // K-steps 0 and 1, whole tiles
-    {
-        DirectLoader<BM, BK, false, 8> la;
-        DirectLoader<BN, BK, B_MN, 8> lb;
-        la.init(sa);
-        lb.init(sb);
-        la.issue(smem, 0);
-        lb.issue(smem + BM * BK, 0);
-        if (nk > 1) {
-            la.issue(smem + STAGE, 1);
-            lb.issue(smem + STAGE + BM * BK, 1);
-        }
+    // group 0 loads A half 0 and B half 1, group 1 B half 0 and A half 1,
+    // K-steps 0 and 1 up front
+    std::conditional_t<A_MN, ColHalfLoaderMN<BK>, HalfLoader<BM, BK>> ha;
+    std::conditional_t<B_MN, HalfLoaderMN<BN, BK>, HalfLoader<BN, BK>> hb;
+    ha.init(sa, lds_addr(smem), g, w4);
+    hb.init(sb, lds_addr(smem + BM * BK), 1 - g, w4);
+    ha.issue(0, 0);
+    hb.issue(0, 0);
+    if (nk > 1) {
+        ha.issue(STAGE * 2, 1);
+        hb.issue(STAGE * 2, 1);
     }
-    // later K-steps: group 0 loads B half 0 and A half 1, group 1 A half 0 and B half 1
-    static_assert(!B_MN, "K-major weights");
-    HalfLoader<BM, BK> ha;
-    HalfLoader<BN, BK> hb;
-    ha.init(sa, lds_addr(smem), g == 0 ? 1 : 0, w4);
-    hb.init(sb, lds_addr(smem + BM * BK), g, w4);
     if (nk > 1) wait_vmcnt<8>();
     else wait_vmcnt<0>();
     __syncthreads();
 
-    bf16x8 af[2][MI], bfr[2][NJ];
-    auto read_hs = [&](int hs) __attribute__((always_inline)) {
+    // fragments of one 16-deep k-slice: 4 A sub-tiles, 2 B sub-tiles
+    struct Slot {
+        bf16x8 a[MI], b[NJ];
+    };
+    // fragment m (A 0..3, B 4..5) of k-slice s2 of half K-step hs
+    auto read_one = [&](int hs, int s2, int m, Slot& dst) __attribute__((always_inline)) {
         const uint16_t* a_s = smem + ((hs >> 1) & 1) * STAGE;
         const uint16_t* b_s = a_s + BM * BK;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int ks = (hs & 1) * 2 + s;
-#pragma unroll
-            for (int i = 0; i < MI; ++i) af[s][i] = read_frag<BM, BK, false>(a_s, g * 128 + i * 32, ks, lane);
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) bfr[s][j] = read_frag<BN, BK, B_MN>(b_s, WL<8>::sub_col(w4, j), ks, lane);
+        const int ks = (hs & 1) * 2 + s2;
+        if (m < MI) {
+            if constexpr (A_MN) dst.a[m] = read_frag<128, BK, true>(a_s + g * 128 * BK, m * 32, ks, lane);
+            else dst.a[m] = read_frag<BM, BK, false>(a_s, g * 128 + m * 32, ks, lane);
         }
+        else dst.b[m - MI] = read_frag<BN, BK, B_MN>(b_s, WL<8>::sub_col(w4, m - MI), ks, lane);
     };
-    auto compute = [&]() __attribute__((always_inline)) {
+    // the 16 MFMAs of k-slices p (first) and c1 (second); with RD, the
+    // fragments of half K-step hs: its second k-slice into n1 during the
+    // first 8 MFMAs, its first k-slice into p (free by then) during the last 8
+    auto compute = [&](auto RD, int hs, Slot& p, Slot& c1, Slot& n1) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);   // ahead of the memory-phase wave of this SIMD
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int n = 0; n < 16; ++n) {
+            const int i = (n >> 1) & 3, j = n & 1;
+            if (n < 8) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(p.b[j], p.a[i], acc[i][j], 0, 0, 0);
+            else acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c1.b[j], c1.a[i], acc[i][j], 0, 0, 0);
+            if constexpr (decltype(RD)::value) {
+                if (n < 6) read_one(hs, 1, n, n1);
+                else if (n >= 8 && n < 14) read_one(hs, 0, n - 8, p);
+            }
+        }
+        if constexpr (decltype(RD)::value) {
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
+            for (int h = 0; h < 2; ++h) {
+                // LDS reads per fragment (a transposed, MN-major one takes two)
+                constexpr int NRA = A_MN ? 2 : 1, NRB = B_MN ? 2 : 1;
 #pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[s][j], af[s][i], acc[i][j], 0, 0, 0);
+                for (int n = 0; n < MI; ++n) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, NRA, 0);
+                }
+#pragma unroll
+                for (int n = 0; n < NJ; ++n) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, NRB, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
+        }
+        __builtin_amdgcn_s_setprio(0);
     };
-    // direct loads of this wave's memory tick t
+    // this wave's direct loads of memory tick t
     auto loads = [&](int t) __attribute__((always_inline)) {
         int j;
         if (g == 0) {
-            if ((t & 3) == 3) {          // B half 0 of K-step j
+            if ((t & 3) == 1) {          // A half 0 of K-step j
+                j = (t + 7) >> 2;
+                if (j >= 2 && j < nk) ha.issue((uint32_t)(j & 1) * STAGE * 2, j);
+            } else {                     // t % 4 == 3: B half 1
                 j = (t + 5) >> 2;
                 if (j >= 2 && j < nk) hb.issue((uint32_t)(j & 1) * STAGE * 2, j);
-            } else {                     // t % 4 == 1: A half 1 (rows 128..255)
-                j = (t + 3) >> 2;
-                if (j >= 2 && j < nk) ha.issue((uint32_t)(j & 1) * STAGE * 2, j);
             }
         } else {
-            if ((t & 3) == 2) {          // A half 0 (rows 0..127)
+            if ((t & 3) == 2) {          // B half 0
                 j = (t + 6) >> 2;
-                if (j >= 2 && j < nk) ha.issue((uint32_t)(j & 1) * STAGE * 2, j);
-            } else {                     // t % 4 == 0: B half 1
-                j = (t >> 2) + 1;
                 if (j >= 2 && j < nk) hb.issue((uint32_t)(j & 1) * STAGE * 2, j);
+            } else {                     // t % 4 == 0: A half 1
+                j = (t + 4) >> 2;
+                if (j >= 2 && j < nk) ha.issue((uint32_t)(j & 1) * STAGE * 2, j);
             }
         }
     };
-    // end of tick t: the loads the next ticks read have landed, then the barrier
+    // end of tick t: what the next tick reads has landed, then the barrier
     auto end_tick = [&](int t) __attribute__((always_inline)) {
-        if ((t & 3) == 2) {
-            // group 0 needs its B half 0 of K-step (t+2)/4 (its A half 1 of that
-            // K-step, issued a tick later, may stay in flight); group 1 its A
-            // half 0 and B half 1 of that K-step (its A half 0 of the next
-            // one, issued this tick, may stay in flight)
-            const int j = g == 0 ? (t + 2) >> 2 : (t + 6) >> 2;
-            if (j >= 2 && j < nk) wait_vmcnt<4>();
+        if ((t & 3) == 1) {
+            // K-step j = (t+3)/4 is read from the next tick on: group 0 needs
+            // its A half 0 and B half 1 (A half 0 of K-step j+1, issued this
+            // tick, may stay in flight), group 1 its B half 0 (A half 1 of
+            // K-step j may stay in flight)
+            const int j = (t + 3) >> 2;
+            const int jn = g == 0 ? j + 1 : j;
+            if (jn >= 2 && jn < nk) wait_vmcnt<4>();
             else wait_vmcnt<0>();
-        } else if ((t & 3) == 3 && g == 0) {
-            // group 0 needs its A half 1 of K-step (t+1)/4 (B half 0 of the
-            // next one, issued this tick, may stay in flight)
-            const int j = (t + 5) >> 2;
-            if (j >= 2 && j < nk) wait_vmcnt<4>();
+        } else if ((t & 3) == 2 && g == 1) {
+            // group 1 reads K-step (t+2)/4 from the next tick on and needs its
+            // A half 1 (B half 0 of the next K-step, issued this tick, may
+            // stay in flight)
+            const int jn = ((t + 2) >> 2) + 1;
+            if (jn >= 2 && jn < nk) wait_vmcnt<4>();
             else wait_vmcnt<0>();
         }
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
     };
+    const std::integral_constant<bool, true> rd;
+    const std::integral_constant<bool, false> no_rd;
+    Slot sp, sq, sr;   // first k-slice; second k-slice, alternating between sq and sr
+    auto read_all = [&](int hs) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < 6; ++m) read_one(hs, 0, m, sp);
+#pragma unroll
+        for (int m = 0; m < 6; ++m) read_one(hs, 1, m, sq);
+    };
 
     if (g == 0) {
-        read_hs(0);
-        for (int u = 0; u < H; ++u) {
-            compute();                       // tick 2u
+        read_all(0);
+        int u = 0;
+        for (; u + 2 < H; u += 2) {
+            compute(rd, u + 1, sp, sq, sr);                  // tick 2u
             end_tick(2 * u);
-            loads(2 * u + 1);                // tick 2u+1
-            if (u + 1 < H) read_hs(u + 1);
+            loads(2 * u + 1);                                // tick 2u+1
             end_tick(2 * u + 1);
+            compute(rd, u + 2, sp, sr, sq);                  // tick 2u+2
+            end_tick(2 * u + 2);
+            loads(2 * u + 3);                                // tick 2u+3
+            end_tick(2 * u + 3);
         }
+        compute(rd, u + 1, sp, sq, sr);                      // tick 2H-4
+        end_tick(2 * u);
+        loads(2 * u + 1);
+        end_tick(2 * u + 1);
+        compute(no_rd, 0, sp, sr, sq);                       // tick 2H-2
+        end_tick(2 * u + 2);
+        loads(2 * u + 3);
+        end_tick(2 * u + 3);
     } else {
-        for (int u = 0; u < H; ++u) {
-            loads(2 * u);                    // tick 2u
-            read_hs(u);
-            end_tick(2 * u);
-            compute();                       // tick 2u+1
+        loads(0);                                            // tick 0
+        read_all(0);
+        end_tick(0);
+        int u = 0;
+        for (; u + 2 < H; u += 2) {
+            compute(rd, u + 1, sp, sq, sr);                  // tick 2u+1
             end_tick(2 * u + 1);
+            loads(2 * u + 2);                                // tick 2u+2
+            end_tick(2 * u + 2);
+            compute(rd, u + 2, sp, sr, sq);                  // tick 2u+3
+            end_tick(2 * u + 3);
+            loads(2 * u + 4);                                // tick 2u+4
+            end_tick(2 * u + 4);
         }
+        compute(rd, u + 1, sp, sq, sr);                      // tick 2H-3
+        end_tick(2 * u + 1);
+        loads(2 * u + 2);
+        end_tick(2 * u + 2);
+        compute(no_rd, 0, sp, sr, sq);                       // tick 2H-1
+        end_tick(2 * u + 3);
     }
 }
 
@@ -456,8 +600,8 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_m_kernel(MParams p)
         }
     }
     f32x16 acc[BM / 64][WL<NW>::NJ];
-    if constexpr (KAL && !B_MN && NW == 8 && BM == 256 && BK == 64 && MOE_GEMM_PINGPONG)
-        mainloop_pp<B_MN>(sa, sb, acc, smem);
+    if constexpr (KAL && NW == 8 && BM == 256 && BK == 64 && MOE_GEMM_PINGPONG)
+        mainloop_pp<false, B_MN>(sa, sb, acc, smem);
     else
         mainloop<BM, BK, NS, false, B_MN, NW, KAL>(sa, sb, acc, smem);
     epilogue_m<BM, EPI, NW>(acc, p, row0, rows_valid, nt, reinterpret_cast<uint8_t*>(smem));
@@ -524,7 +668,10 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_kernel(KParams p)
     sb.K = m_e;
 
     f32x16 acc[BM / 64][WL<NW>::NJ];
-    mainloop<BM, BK, NS, true, true, NW, true>(sa, sb, acc, smem);
+    if constexpr (NW == 8 && BM == 256 && BK == 64 && MOE_GEMM_PINGPONG_K)
+        mainloop_pp<true, true>(sa, sb, acc, smem);
+    else
+        mainloop<BM, BK, NS, true, true, NW, true>(sa, sb, acc, smem);
 
     store_tile<BM, NW>(acc, q.C + (int64_t)e * q.sC + (int64_t)mt * BM * q.ldc, q.ldc, q.M - mt * BM, nt * BN,
                    q.N, reinterpret_cast<uint8_t*>(smem));
