@@ -536,12 +536,10 @@ template <int BM, int BK, int NS, bool B_MN, int EPI, int NW, bool KAL>
 __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_m_kernel(MParams p)
 {
     __shared__ __align__(16) uint16_t smem[NS * (BM + BN) * BK];
-    __shared__ int s_pref[kMaxExperts + 1];
-    __shared__ int s_part[64 * NW];
 
     // device tile schedule: expert-major, N-tile, then M-tile
     MTile tile;
-    if (!schedule_m<BM, 64 * NW>(p.group_off, p.capacity, p.E, p.n_rows, p.ntn, s_pref, s_part, tile)) return;
+    if (!schedule_m<BM>(p.group_off, p.capacity, p.E, p.n_rows, p.ntn, tile)) return;
     const int e = tile.e, nt = tile.nt;
     const int64_t row0 = tile.row0;
     const int rows_valid = tile.rows_valid;

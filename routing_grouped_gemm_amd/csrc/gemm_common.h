@@ -448,8 +448,10 @@ __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][WL<NW>::
                                                amdgpu_flat_work_group_size(64 * (NW), 64 * (NW))))
 
 
-// Device tile schedule of a grouped-M launch: every workgroup builds the
-// prefix over experts of ceil(m_e / BM) * ntn tiles in LDS, remaps its id so
+// Device tile schedule of a grouped-M launch: every wave of a workgroup
+// sums, lane by lane, the ceil(m_e / BM) * ntn tiles of the experts (lane l
+// takes experts l*per .. l*per+per-1, per = ceil(E / 64)) and scans the lane
+// sums across the wave (no LDS, no barrier), remaps the workgroup id so
 // that a contiguous range of tiles lands on one XCD, and finds its expert,
 // N-tile and M-tile.  Returns false for surplus workgroups.
 struct MTile {
@@ -457,23 +459,48 @@ struct MTile {
     int64_t row0;
 };
 
-template <int BM, int NT>
-__device__ __forceinline__ bool schedule_m(const int32_t* group_off, int capacity, int E,
-                                           int64_t n_rows, int ntn, int* s_pref, int* s_part,
-                                           MTile& t)
+template <int BM>
+__device__ __forceinline__ bool schedule_m(const int32_t* group_off, int capacity, int E, int64_t n_rows,
+                                           int ntn, MTile& t)
 {
-    const int total = block_tile_prefix<NT>(group_off, capacity, E, n_rows, BM, ntn, s_pref, s_part);
+    const int lane = threadIdx.x & 63;
+    const int per = (E + 63) >> 6;   // experts per lane (at most 16)
+    const int gb = lane * per;
+    auto tiles = [&](int g) __attribute__((always_inline)) {
+        return (int)((group_rows(group_off, capacity, g, n_rows) + BM - 1) / BM) * ntn;
+    };
+    int cnt = 0;
+    for (int k = 0; k < per && gb + k < E; ++k) cnt += tiles(gb + k);
+    int incl = cnt;   // inclusive scan of the lane sums
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    const int total = __builtin_amdgcn_readlane(incl, 63);   // wave-uniform
     const int per_xcd = (total + 7) / 8;
     const int xcd = blockIdx.x % 8;
     const int slot = blockIdx.x / 8;
     if (slot >= per_xcd) return false;
     const int L = xcd * per_xcd + slot;
     if (L >= total) return false;
-    t.e = find_group(s_pref, E, L);
+    // the one lane whose experts hold tile L, then the expert within it
+    const int excl = incl - cnt;
+    const int src = __ffsll((unsigned long long)__ballot(excl <= L && L < incl)) - 1;
+    int e = gb, first = excl;
+    for (int k = 0, run = excl; k < per && gb + k < E; ++k) {
+        const int c = tiles(gb + k);
+        if (L >= run && L < run + c) {
+            e = gb + k;
+            first = run;
+        }
+        run += c;
+    }
+    t.e = __builtin_amdgcn_readlane(e, src);
+    const int local = L - __builtin_amdgcn_readlane(first, src);
     const int64_t g0 = group_begin(group_off, capacity, t.e, n_rows);
     const int m_e = (int)group_rows(group_off, capacity, t.e, n_rows);
     const int mt_e = (m_e + BM - 1) / BM;
-    const int local = L - s_pref[t.e];
     t.nt = local / mt_e;
     t.mt = local - t.nt * mt_e;
     t.row0 = g0 + (int64_t)t.mt * BM;

@@ -198,11 +198,9 @@ template <int BM, int EPI>
 __global__ MOE_GEMM_KERNEL_ATTRS void mx_grouped_m_kernel(MxMParams mp)
 {
     __shared__ __align__(16) uint8_t smem[MNS * ((BM + BN) * MBK + (BM + BN) * 4)];
-    __shared__ int s_pref[kMaxExperts + 1];
-    __shared__ int s_part[NTH];
     const MParams& p = mp.p;
     MTile tile;
-    if (!schedule_m<BM, NTH>(p.group_off, p.capacity, p.E, p.n_rows, p.ntn, s_pref, s_part, tile)) return;
+    if (!schedule_m<BM>(p.group_off, p.capacity, p.E, p.n_rows, p.ntn, tile)) return;
     const int e = tile.e, nt = tile.nt;
     const int64_t K = p.K;
 
