@@ -303,16 +303,26 @@ __device__ __forceinline__ void stage_put(uint8_t* lds, uint32_t off, uint2 v)
     *reinterpret_cast<uint2*>(lds + off) = v;
 }
 
-// After a barrier: thread t hands out chunks t, t + NTH, ... as put(r, c, v);
-// a trailing barrier frees the LDS again.
+// After a barrier: thread t hands out chunks t, t + NTH, ... as put(r, c, v),
+// all of its LDS reads first (one wait instead of one per chunk); a
+// trailing barrier frees the LDS again.
 template <int ROWS, int CH, int NT = NTH, class F>
 __device__ __forceinline__ void stage_flush(const uint8_t* lds, F&& put)
 {
+    constexpr int N = ROWS * CH / NT;   // chunks per thread
+    static_assert(ROWS * CH % NT == 0, "whole chunks per thread");
     __syncthreads();
-#pragma unroll 4
-    for (int q = threadIdx.x; q < ROWS * CH; q += NT) {
+    uint4 v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int q = (int)threadIdx.x + i * NT;
         const int r = q / CH, c = q % CH;
-        put(r, c, *reinterpret_cast<const uint4*>(lds + r * (CH * 16) + ((c ^ (r & (CH - 1))) << 4)));
+        v[i] = *reinterpret_cast<const uint4*>(lds + r * (CH * 16) + ((c ^ (r & (CH - 1))) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int q = (int)threadIdx.x + i * NT;
+        put(q / CH, q % CH, v[i]);
     }
     __syncthreads();
 }
@@ -424,14 +434,25 @@ __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][WL<NW>::
                         stage_put(lu, off, pack4_bf16(duv[0], duv[1], duv[2], duv[3]));
                     }
             __syncthreads();
-#pragma unroll 4
-            for (int q = threadIdx.x; q < BM * 16 * 2; q += NT) {
+            // both tiles out as rows of dgu, all LDS reads of a thread first
+            constexpr int NQ = BM * 16 * 2 / NT;
+            static_assert(BM * 16 * 2 % NT == 0, "whole chunks per thread");
+            uint4 v[NQ];
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int q = (int)threadIdx.x + i * NT;
+                const int which = q / (BM * 16), qq = q % (BM * 16);
+                const int r = qq >> 4, c = qq & 15;
+                v[i] = *reinterpret_cast<const uint4*>((which ? lu : lg) + r * 256 + ((c ^ (r & 15)) << 4));
+            }
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int q = (int)threadIdx.x + i * NT;
                 const int which = q / (BM * 16), qq = q % (BM * 16);
                 const int r = qq >> 4, c = qq & 15;
                 const int n = nc + 8 * c;
-                const uint4 v = *reinterpret_cast<const uint4*>((which ? lu : lg) + r * 256 + ((c ^ (r & 15)) << 4));
                 if (r < rows_valid && n < p.N)
-                    *reinterpret_cast<uint4*>(p.C + (row0 + r) * p.ldc + (which ? p.f + n : n)) = v;
+                    *reinterpret_cast<uint4*>(p.C + (row0 + r) * p.ldc + (which ? p.f + n : n)) = v[i];
             }
             __syncthreads();
         }
