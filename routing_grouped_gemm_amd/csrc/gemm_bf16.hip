@@ -38,6 +38,11 @@
 // the same loop for the weight-gradient GEMM (both operands MN-major, every
 // fragment two transposed LDS reads); measured about 5% slower there than the
 // single-group loop at 256 x 256 tiles over experts of ~512 rows
+// single-group loop with both operands MN-major (the weight gradient): the
+// next k-slice's fragment reads go between the MFMAs instead of in a burst
+#ifndef MOE_GEMM_READ_INTERLEAVE
+#define MOE_GEMM_READ_INTERLEAVE 1
+#endif
 #ifndef MOE_GEMM_PINGPONG_K
 #define MOE_GEMM_PINGPONG_K 0
 #endif
@@ -165,6 +170,31 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
                     }
             }
     };
+    // RI: slice() with the fragments of k-slice ks of the stage at (a_s, b_s)
+    // read into buffer rb between its MFMAs (fragment n after MFMA n), in
+    // place of a burst of reads ahead of the slice
+    auto slice_rd = [&](int buf, int m0, auto&& load, int rb, const uint16_t* a_s, const uint16_t* b_s,
+                        int ks) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][j], af[buf][i], acc[i][j], 0, 0, 0);
+                const int n = i * NJ + j;
+                if (n < MI) af[rb][n] = read_frag<BM, BK, A_MN>(a_s, wm * (BM / 2) + n * 32, ks, lane);
+                else if (n < MI + NJ)
+                    bfr[rb][n - MI] = read_frag<BN, BK, B_MN>(b_s, WL<NW>::sub_col(wn, n - MI), ks, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                const int m = m0 + n;
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    if ((q + 1) * SPAN / NQ - 1 == m) {
+                        load(q);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+            }
+    };
+    constexpr bool RI = MOE_GEMM_READ_INTERLEAVE && A_MN && B_MN && MI * NJ >= MI + NJ;
 
     // one K-step.  MODE 1: the next K-step lies inside K (or is masked past K
     // by the descriptors), so its loads go out without the K-tail test;
@@ -186,21 +216,29 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
                 else lb.issue_one(nxt + BM * BK, kt + 1, q - NA);
             }
         };
-        read(0, a_s, b_s, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (kt > 0) {
-            slice(1, 0, load);   // the last k-slice of K-step kt-1
+        if (RI && kt > 0) {
+            slice_rd(1, 0, load, 0, a_s, b_s, 0);   // the last k-slice of K-step kt-1
         } else {
+            read(0, a_s, b_s, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt > 0) {
+                slice(1, 0, load);   // the last k-slice of K-step kt-1
+            } else {
 #pragma unroll
-            for (int q = 0; q < NQ; ++q)
-                if ((q + 1) * SPAN / NQ - 1 < SM) load(q);
+                for (int q = 0; q < NQ; ++q)
+                    if ((q + 1) * SPAN / NQ - 1 < SM) load(q);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks + 1 < KS; ++ks) {
-            read((ks + 1) & 1, a_s, b_s, ks + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            slice(ks & 1, (ks + 1) * SM, load);
+            if constexpr (RI) {
+                slice_rd(ks & 1, (ks + 1) * SM, load, (ks + 1) & 1, a_s, b_s, ks + 1);
+            } else {
+                read((ks + 1) & 1, a_s, b_s, ks + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                slice(ks & 1, (ks + 1) * SM, load);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
