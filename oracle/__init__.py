@@ -58,6 +58,8 @@ def _load():
     lib.oracle_route.restype = I
     lib.oracle_permute.argtypes = [P, I, I, I, P, P, L, I, P]
     lib.oracle_combine.argtypes = [P, P, P, I, I, I, I, P]
+    lib.oracle_router_logits.argtypes = [P, P, I, I, I, I, P]
+    lib.oracle_gate_grad.argtypes = [P, P, P, P, P, I, I, I, I, I, P, P]
     lib.oracle_ffn_fwd.argtypes = [P, P, P, P, I, I, I, I, I, P, P, P]
     lib.oracle_ffn_bwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, P, P, P, P, P, I,
                                    P, P, P, P]
@@ -159,6 +161,34 @@ def combine(y_perm, dst_row, w, T, k, round_mode=NONE):
     ww = None if w is None else _f32(w).reshape(-1)
     _load().oracle_combine(_p(y), _p(_i32(dst_row)), _p(ww), T, k, d, round_mode, _p(out))
     return out
+
+
+# ---------------------------------------------------------------- router
+def router_logits(x, w_r, round_mode=FP32):
+    """Router scores [T, E] = x [T, d] . w_r [E, d]^T (fp64 sums, stored per round_mode)."""
+    x = _f64(x)
+    w = _f64(w_r)
+    T, d = x.shape
+    E = w.shape[0]
+    assert w.shape == (E, d)
+    out = np.empty((T, E))
+    _load().oracle_router_logits(_p(x), _p(w), T, E, d, round_mode, _p(out))
+    return out
+
+
+def gate_grad(dout, y_perm, dst_row, topk_idx, topk_w, E, round_mode=FP32):
+    """Gradient through the gate weights.  Returns (dw [T, k] fp64, dlogits [T, E])."""
+    g = _f64(dout)
+    y = _f64(y_perm)
+    idx = _i32(topk_idx)
+    T, k = idx.shape
+    d = g.shape[1]
+    assert y.shape[1] == d
+    dw = np.empty((T, k))
+    dl = np.empty((T, E))
+    _load().oracle_gate_grad(_p(g), _p(y), _p(_i32(dst_row)), _p(idx), _p(_f32(topk_w)), T, E, k, d,
+                             round_mode, _p(dw), _p(dl))
+    return dw, dl
 
 
 # ---------------------------------------------------------------- expert FFN

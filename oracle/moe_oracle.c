@@ -208,6 +208,61 @@ ORACLE_API void oracle_combine(const double* y_perm, const int32_t* dst_row, con
 }
 
 /* ------------------------------------------------------------------ */
+/* Router scores and the gradient through the gate weights              */
+/* ------------------------------------------------------------------ */
+
+/* Router scores: logits[t,e] = sum_i x[t,i] * w_r[e,i], accumulated in
+ * fp64 and stored with round_mode.  The layer stores them in fp32: the
+ * tutorial's MXFP8 section (the DeepSeek-V3 paragraph) keeps the gating
+ * in high precision.  Reading: a bias-free linear router over the token's
+ * d features, weights [E, d] (the pages do not spell the router out). */
+ORACLE_API void oracle_router_logits(const double* x, const double* w_r, int T, int E, int d,
+                                     int round_mode, double* logits)
+{
+    #pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t)
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i) acc += x[(long)t * d + i] * w_r[(long)e * d + i];
+            logits[(long)t * E + e] = round_store(acc, round_mode);
+        }
+}
+
+/* Gradient of the layer output through the gate weights, back to the
+ * router scores.  The combine gives out[t] = sum_j w[t,j] * y_perm[dst(t,j)]
+ * over the non-dropped slots, so dw[t,j] = sum_i dout[t,i] *
+ * y_perm[dst(t,j), i], and 0 for a dropped slot (it adds nothing to out).
+ * The gate weights are the softmax over the k selected logits (the reading
+ * the route takes), w_j = exp(l_j) / sum_m exp(l_m), whose Jacobian gives
+ * dlogits[t, topk_idx[t,j]] = w[t,j] * (dw[t,j] - sum_m w[t,m] dw[t,m]);
+ * the logits of the experts not selected get 0 (the selection is piecewise
+ * constant in them).  fp64 throughout; dw kept in fp64, dlogits [T, E]
+ * stored with round_mode. */
+ORACLE_API void oracle_gate_grad(const double* dout, const double* y_perm, const int32_t* dst_row,
+                                 const int32_t* topk_idx, const float* w, int T, int E, int k,
+                                 int d, int round_mode, double* dw, double* dlogits)
+{
+    #pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            long p = (long)t * k + j;
+            long dst = dst_row[p];
+            double acc = 0.0;
+            if (dst >= 0)
+                for (int i = 0; i < d; ++i) acc += dout[(long)t * d + i] * y_perm[dst * d + i];
+            dw[p] = acc;
+        }
+        double wdw = 0.0;
+        for (int m = 0; m < k; ++m) wdw += (double)w[(long)t * k + m] * dw[(long)t * k + m];
+        for (int e = 0; e < E; ++e) dlogits[(long)t * E + e] = 0.0;
+        for (int j = 0; j < k; ++j) {
+            long p = (long)t * k + j;
+            dlogits[(long)t * E + topk_idx[p]] = round_store((double)w[p] * (dw[p] - wdw), round_mode);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* Expert SwiGLU FFN over contiguous groups of rows                     */
 /* ------------------------------------------------------------------ */
 
