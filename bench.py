@@ -232,8 +232,39 @@ def run_gpu(args, cfg):
     gpu_ms = sum(evs[i][0].elapsed_time(evs[i][len(STAGES)]) for i in range(K)) / K
     ms_per_step = wall * 1e3 / K
     counts = lay.counts.cpu()
-    return dict(stage_ms=stage_ms, gpu_ms=gpu_ms, ms_per_step=ms_per_step, R=R, cap=cap,
+    f1 = router_steps(lay, inp, K) if dt == m.MOE_BF16 and not cap else None
+    return dict(stage_ms=stage_ms, gpu_ms=gpu_ms, ms_per_step=ms_per_step, R=R, cap=cap, f1=f1,
                 counts=counts, inp=inp, lay=lay)
+
+
+def router_steps(lay, inp, reps):
+    """The steps either side of the layer (not part of the timed step): router
+    scores x . W_r^T and the gradient through the gate weights (dlogits), each
+    timed alone over `reps` launches after the layer's own step, on the same
+    synthetic inputs (the gate gradient reads the last forward's expert
+    outputs).  Returns {name: {"ms", "gbs", "frac_hbm", "bytes"}}."""
+    import torch
+    T, d, E, k, R = lay.T, lay.d, lay.E, lay.k, lay.n_rows
+    work = {
+        "router_logits": (lambda: lay.router_scores(inp["x"], inp["w_router"]),
+                          T * d * 2 + E * d * 2 + T * E * 4),
+        "gate_grad": (lambda: lay.gate_grad(inp["dout"]), T * d * 2 + R * d * 2 + T * E * 4 + T * k * 12),
+    }
+    out = {}
+    for name, (fn, by) in work.items():
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        out[name] = {"ms": round(ms, 4), "gbs": round(by / ms / 1e6, 1),
+                     "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4), "bytes": by}
+    return out
 
 
 def cpu_baseline(args, cfg, inp):
@@ -376,6 +407,8 @@ def main():
         "roofline": rl,
         "expert_rows": {"min": int(res["counts"].min()), "max": int(res["counts"].max())},
     }
+    if res["f1"]:
+        out["router_and_gate_grad"] = res["f1"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, cfg, res["inp"])
     print(json.dumps(out), flush=True)

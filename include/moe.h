@@ -278,6 +278,49 @@ MOE_API int moe_quantize_mxfp8(const void* src, int64_t rows, int K, int colwise
                        const int32_t* group_off, int n_groups, uint8_t* codes,
                        uint8_t* scales, moe_stream_t stream);
 
+/*
+ * Router scores, the step before moe_route_topk:
+ *   logits[t, e] = sum_i x[t, i] * w_router[e, i]
+ * bf16 operands, fp32 accumulation and fp32 result (the tutorial's MXFP8
+ * section keeps the gating in high precision; the pages do not spell the
+ * router out, and this is the plainest reading: a bias-free linear map).
+ * in   x          [T, d] bf16, 16-byte aligned, d % 8 == 0.
+ * in   w_router   [E, d] bf16, 16-byte aligned; 1 <= E <= 1024.
+ * out  logits     [T, E] fp32, 16-byte aligned.
+ * Errors: MOE_EINVAL (sizes, null pointers), MOE_EALIGN (d % 8, alignment).
+ */
+MOE_API int moe_router_logits(const void* x, const void* w_router, int T, int E, int d,
+                              float* logits, moe_stream_t stream);
+
+/*
+ * Gradient through the gate weights, back to the router scores (the
+ * backward of the weighted combine with respect to its weights, then of the
+ * softmax over the k selected logits that moe_route_topk forms):
+ *   dw[t, j]                  = <dout[t], y_perm[dst_row[t*k+j]]>  (0 for a dropped slot)
+ *   dlogits[t, topk_idx[t,j]] = topk_w[t,j] * (dw[t,j] - sum_m topk_w[t,m] * dw[t,m])
+ *   dlogits[t, e]             = 0 for the experts not selected
+ * with the dot products accumulated in fp32.
+ * in   dout       [T, d] bf16 (upstream gradient of the layer output).
+ * in   y_perm     [n_rows, d] bf16 (the expert outputs of the forward).
+ * in   topk_idx, topk_w, dst_row  [T, k], as moe_route_topk wrote them.
+ * out  dlogits    [T, E] fp32, every entry written.
+ * out  dw         [T, k] fp32, optional (NULL: not written).
+ * out  dy_perm    [n_rows, d] bf16, optional: also writes the combine
+ *                 backward dy_perm[dst] = topk_w * dout[t] (what moe_permute
+ *                 with row_scale = topk_w writes) from the same dout reads.
+ *                 Unpadded layouts only (n_rows == T*k): MOE_EUNSUPPORTED
+ *                 otherwise, as padding rows would stay unwritten.
+ * out  dev_err    optional; MOE_ERR_ROW_RANGE for a destination >= n_rows
+ *                 (that slot is then treated as dropped).
+ * Errors: MOE_EINVAL (sizes: 1 <= k <= 8, k <= E <= 1024; null pointers),
+ * MOE_EALIGN (d % 8, 16-byte alignment of dout, y_perm, dy_perm, dlogits),
+ * MOE_EUNSUPPORTED (dy_perm with a padded layout).
+ */
+MOE_API int moe_gate_grad(const void* dout, const void* y_perm, const int32_t* topk_idx,
+                          const float* topk_w, const int32_t* dst_row, int T, int E, int k, int d,
+                          int64_t n_rows, float* dlogits, float* dw, void* dy_perm,
+                          int32_t* dev_err, moe_stream_t stream);
+
 /* Static text naming a status code. */
 MOE_API const char* moe_status_string(int status);
 

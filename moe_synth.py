@@ -101,6 +101,9 @@ def make_inputs(name=None, device="cpu", seed=None, act_dtype=None, **over):
     out["w13"] = normal((E, 2 * f, d), 0.02, s + 3, device, act_dtype)
     out["w2"] = normal((E, d, f), 0.02, s + 4, device, act_dtype)
     out["dout"] = normal((T, d), 1.0, s + 5, device, act_dtype)
+    # router weights [E, d]: std 1 / (0.02 sqrt(d)), so that with x ~ N(0, 0.02)
+    # the router scores x . W_r^T are about N(0, 1) like the logits above
+    out["w_router"] = normal((E, d), 1.0 / (0.02 * math.sqrt(d)), s + 7, device, act_dtype)
     if cfg.get("gate") == "uniform01":
         out["gate"] = uniform01((T,), s + 6, device)
     return out

@@ -24,7 +24,7 @@ MOE_GEMM_GATE_UP, MOE_GEMM_DOWN, MOE_GEMM_DGRAD_DOWN, MOE_GEMM_DGRAD_GATE_UP, MO
 ABI_FUNCTIONS = ("moe_route_workspace_bytes", "moe_route_topk", "moe_permute",
                  "moe_gemm_workspace_bytes", "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd",
                  "moe_grouped_gemm_op", "moe_unpermute_combine", "moe_quantize_mxfp8",
-                 "moe_status_string", "moe_version")
+                 "moe_router_logits", "moe_gate_grad", "moe_status_string", "moe_version")
 
 GEMM_TENSOR_FIELDS = ("x_perm", "x_perm_scales", "w13", "w13_scales", "w2", "w2_scales", "gu",
                       "h", "y_perm", "dy_perm", "dgu", "dx_perm", "dw13", "dw2", "ws")
@@ -80,6 +80,10 @@ def load():
     lib.moe_unpermute_combine.argtypes = [I, P, P, P, I, I, I, I64, P, P, P]
     lib.moe_quantize_mxfp8.restype = I
     lib.moe_quantize_mxfp8.argtypes = [P, I64, I, I, P, I, P, P, P]
+    lib.moe_router_logits.restype = I
+    lib.moe_router_logits.argtypes = [P, P, I, I, I, P, P]
+    lib.moe_gate_grad.restype = I
+    lib.moe_gate_grad.argtypes = [P, P, P, P, P, I, I, I, I, I64, P, P, P, P, P]
     _lib = lib
     return lib
 
@@ -207,6 +211,27 @@ def moe_unpermute_combine(dtype, y_perm, dst_row, weights, k, out, dev_err=None,
     rc = load().moe_unpermute_combine(dtype, _p(y_perm), _p(dst_row), _p(weights), T, k, d,
                                       n_rows, _p(out), _p(dev_err), _s(stream))
     _check(rc, "moe_unpermute_combine")
+
+
+def moe_router_logits(x, w_router, logits, stream=None):
+    """logits [T, E] fp32 = x [T, d] bf16 . w_router [E, d] bf16 ^T."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    rc = load().moe_router_logits(_p(x), _p(w_router), T, E, d, _p(logits), _s(stream))
+    _check(rc, "moe_router_logits")
+
+
+def moe_gate_grad(dout, y_perm, topk_idx, topk_w, dst_row, dlogits, dw=None, dy_perm=None,
+                  dev_err=None, stream=None):
+    """dlogits [T, E] (and optionally dw [T, k], and the combine backward into dy_perm)
+    from dout [T, d] and the forward's expert outputs y_perm [n_rows, d]."""
+    T, d = dout.shape
+    k = topk_idx.shape[1]
+    E = dlogits.shape[1]
+    n_rows = y_perm.shape[0]
+    rc = load().moe_gate_grad(_p(dout), _p(y_perm), _p(topk_idx), _p(topk_w), _p(dst_row), T, E, k, d,
+                              n_rows, _p(dlogits), _p(dw), _p(dy_perm), _p(dev_err), _s(stream))
+    _check(rc, "moe_gate_grad")
 
 
 def moe_quantize_mxfp8(src, colwise, codes, scales, group_off=None, n_groups=0, stream=None):

@@ -713,6 +713,105 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_kernel(KParams p)
                    q.N, reinterpret_cast<uint8_t*>(smem));
 }
 
+// Router scores: logits [T, E] fp32 = x [T, d] . W_r [E, d]^T, bf16 operands,
+// fp32 accumulate (the gating stays in high precision: tutorial, MXFP8
+// section).  A skinny product (E = 128 at most per tile, K = d): the T x d
+// activations stream from HBM once and set the pace.  A workgroup of 4
+// waves owns 64 rows x 128 experts (each wave 32 x 64), with the x and W_r
+// K-steps of 64 moving HBM/L2 -> LDS by direct loads through a 3-stage ring
+// (two K-steps in flight while one is read; a 6-stage ring measured no
+// faster).  The scores leave straight
+// from the accumulators, four consecutive fp32 columns per lane.
+constexpr int kRM = 64, kRN = 128, kRK = 64, kRS = 3;
+
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ w, int T, int E,
+                                                            int d, float* __restrict__ logits)
+{
+    constexpr int STAGE = (kRM + kRN) * kRK;   // elements per stage
+    __shared__ __align__(16) uint16_t smem[kRS * STAGE];
+    const int row0 = blockIdx.x * kRM;
+    const int n0 = blockIdx.y * kRN;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = wave >> 1, wn = wave & 1;   // rows wm*32 .., experts wn*64 ..
+    TileSrc sa;
+    sa.p0 = x + (int64_t)row0 * d;
+    sa.p1 = sa.p0 + (int64_t)(kRM / 2) * d;
+    sa.ld = d;
+    sa.rows0 = max(min(T - row0, kRM / 2), 0);
+    sa.rows1 = max(min(T - row0 - kRM / 2, kRM / 2), 0);
+    sa.K = d;
+    TileSrc sb;
+    sb.p0 = w + (int64_t)n0 * d;
+    sb.p1 = sb.p0 + (int64_t)(kRN / 2) * d;
+    sb.ld = d;
+    sb.rows0 = max(min(E - n0, kRN / 2), 0);
+    sb.rows1 = max(min(E - n0 - kRN / 2, kRN / 2), 0);
+    sb.K = d;
+    DirectLoader<kRM, kRK, false, 4> la;
+    DirectLoader<kRN, kRK, false, 4> lb;
+    la.init(sa);
+    lb.init(sb);
+    constexpr int NQ = DirectLoader<kRM, kRK, false, 4>::PER_WAVE + DirectLoader<kRN, kRK, false, 4>::PER_WAVE;
+    const int nk = (d + kRK - 1) / kRK;
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+        uint16_t* st = smem + (kt % kRS) * STAGE;
+        la.issue(st, kt);
+        lb.issue(st + kRM * kRK, kt);
+    };
+    static_assert(kRS >= 2 && kRS <= 6, "the waits below cover up to four later K-steps");
+    f32x16 acc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+    for (int kt = 0; kt < kRS - 1 && kt < nk; ++kt) issue(kt);
+    for (int kt = 0; kt < nk; ++kt) {
+        // K-step kt has landed once at most the loads of the K-steps issued
+        // after it (up to kRS - 2 of them) are outstanding
+        switch (min(nk - 1 - kt, kRS - 2)) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<NQ>(); break;
+        case 2: wait_vmcnt<2 * NQ>(); break;
+        case 3: wait_vmcnt<3 * NQ>(); break;
+        default: wait_vmcnt<4 * NQ>(); break;
+        }
+        __syncthreads();   // everyone's loads of kt landed; K-step kt-1's stage is free
+        if (kt + kRS - 1 < nk) issue(kt + kRS - 1);
+        const uint16_t* a_s = smem + (kt % kRS) * STAGE;
+        const uint16_t* b_s = a_s + kRM * kRK;
+#pragma unroll
+        for (int ks = 0; ks < kRK / 16; ++ks) {
+            const bf16x8 af = read_frag<kRM, kRK, false>(a_s, wm * 32, ks, lane);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const bf16x8 bf = read_frag<kRN, kRK, false>(b_s, wn * 64 + j * 32, ks, lane);
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af, acc[j], 0, 0, 0);
+            }
+        }
+    }
+    // acc[j] holds the transposed 32 x 32 block (rows wm*32.., experts
+    // wn*64 + 32j ..): lane l has row (l & 31) and, for g = 0..3, the four
+    // experts 8g + 4(l >> 5) + {0..3}
+    const int r = row0 + wm * 32 + (lane & 31);
+    if (r >= T) return;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int c = n0 + wn * 64 + j * 32 + 8 * g + 4 * (lane >> 5);
+            float* dst = logits + (int64_t)r * E + c;
+            if ((E & 3) == 0 && c + 3 < E) {
+                *reinterpret_cast<float4*>(dst) =
+                    make_float4(acc[j][4 * g], acc[j][4 * g + 1], acc[j][4 * g + 2], acc[j][4 * g + 3]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (c + q < E) dst[q] = acc[j][4 * g + q];
+            }
+        }
+}
+
 template <int BM, int BK, int NS, bool B_MN, int EPI, int NW>
 hipError_t launch_m(const MParams& p, int64_t n_rows, hipStream_t s)
 {
@@ -764,6 +863,15 @@ constexpr int kNS = MOE_GEMM_NS;     // LDS pipeline stages
 constexpr int kNW = MOE_GEMM_WAVES;  // waves per workgroup (4: one per SIMD, 8: two)
 
 }  // namespace
+
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w, int T, int E, int d, float* logits,
+                                hipStream_t s)
+{
+    if (T == 0) return hipSuccess;
+    const dim3 grid((unsigned)((T + kRM - 1) / kRM), (unsigned)((E + kRN - 1) / kRN));
+    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, s, x, w, T, E, d, logits);
+    return hipGetLastError();
+}
 
 hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, int f,
                         hipStream_t s)

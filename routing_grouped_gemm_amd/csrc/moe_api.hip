@@ -266,6 +266,35 @@ int moe_grouped_gemm_op(int op, int dtype, const moe_gemm_tensors* t,
     return run_gemm_op(op, dtype, *t, g, d, f, as_stream(stream));
 }
 
+int moe_router_logits(const void* x, const void* w_router, int T, int E, int d, float* logits,
+                      moe_stream_t stream)
+{
+    if (T < 0 || T >= kMaxRows || E < 1 || E > kMaxExperts || d < 1) return MOE_EINVAL;
+    if (T > 0 && (!x || !w_router || !logits)) return MOE_EINVAL;
+    if ((int64_t)T * d >= ((int64_t)1 << 40)) return MOE_EINVAL;
+    if (d % 8) return MOE_EALIGN;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(logits)) return MOE_EALIGN;
+    return status_of(launch_router_logits((const uint16_t*)x, (const uint16_t*)w_router, T, E, d, logits,
+                                          as_stream(stream)));
+}
+
+int moe_gate_grad(const void* dout, const void* y_perm, const int32_t* topk_idx, const float* topk_w,
+                  const int32_t* dst_row, int T, int E, int k, int d, int64_t n_rows, float* dlogits,
+                  float* dw, void* dy_perm, int32_t* dev_err, moe_stream_t stream)
+{
+    if (T < 0 || k < 1 || k > kMaxTopK || E < k || E > kMaxExperts || d < 1 || n_rows < 0 ||
+        n_rows >= kMaxRows || (int64_t)T * k >= kMaxRows)
+        return MOE_EINVAL;
+    if (T > 0 && (!dout || !topk_idx || !topk_w || !dst_row || !dlogits)) return MOE_EINVAL;
+    if (T > 0 && n_rows > 0 && !y_perm) return MOE_EINVAL;
+    if (d % 8) return MOE_EALIGN;
+    if (!aligned16(dout) || !aligned16(y_perm) || !aligned16(dy_perm) || !aligned16(dlogits))
+        return MOE_EALIGN;
+    if (dy_perm && n_rows != (int64_t)T * k) return MOE_EUNSUPPORTED;
+    return status_of(launch_gate_grad(dout, y_perm, topk_idx, topk_w, dst_row, T, E, k, d, n_rows, dlogits,
+                                      dw, dy_perm, dev_err, as_stream(stream)));
+}
+
 int moe_quantize_mxfp8(const void* src, int64_t rows, int K, int colwise, const int32_t* group_off,
                        int n_groups, uint8_t* codes, uint8_t* scales, moe_stream_t stream)
 {

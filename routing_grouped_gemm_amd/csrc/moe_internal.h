@@ -160,6 +160,14 @@ hipError_t launch_dequant_requant_cols(const uint8_t* codes_row, const uint8_t* 
                                        int capacity, int n_groups, uint8_t* codes,
                                        uint8_t* scales, hipStream_t stream);
 
+// router scores and the gradient through the gate weights
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w, int T, int E, int d, float* logits,
+                                hipStream_t s);
+hipError_t launch_gate_grad(const void* dout, const void* y_perm, const int32_t* topk_idx,
+                            const float* topk_w, const int32_t* dst_row, int T, int E, int k, int d,
+                            int64_t n_rows, float* dlogits, float* dw, void* dy_perm, int32_t* dev_err,
+                            hipStream_t stream);
+
 // grouped GEMMs (bf16 MFMA, fp32 SIMT, MXFP8 MFMA)
 struct GroupSpec {
     const int32_t* group_off;  // [E+1] device, or nullptr with capacity > 0

@@ -402,6 +402,90 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     if (bad && dev_err) atomicOr(dev_err, (int)MOE_ERR_ROW_RANGE);
 }
 
+// Gradient through the gate weights (the backward of the weighted combine
+// with respect to the weights, then the softmax over the selected logits):
+// one wave per token.  Lane i takes the 16-byte vectors i, i + 64, ... of
+// the token's dout row and of its K expert rows y_perm[dst]; the K partial
+// dot products are summed across the wave; then, with dw_j = <dout, y_j>
+// (0 for a dropped slot), dlogits[t, topk_idx[t,j]] = w_j (dw_j - sum_m w_m
+// dw_m) and every other entry of the token's row is 0.  FUSE also writes
+// the combine backward, dy_perm[dst] = w_j * dout (as the row-scaled permute
+// does), from the dout vectors already in registers.
+template <int K, bool FUSE>
+__global__ __launch_bounds__(256) void gate_grad_kernel(const uint4* __restrict__ dout,
+                                                        const uint4* __restrict__ y, int T, int E,
+                                                        int nvec, const int32_t* __restrict__ topk_idx,
+                                                        const float* __restrict__ topk_w,
+                                                        const int32_t* __restrict__ dst_row,
+                                                        int64_t n_rows, float* __restrict__ dlogits,
+                                                        float* __restrict__ dw_out,
+                                                        uint4* __restrict__ dy_perm,
+                                                        int32_t* __restrict__ dev_err)
+{
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;   // wave-uniform
+    const int lane = threadIdx.x & 63;
+    int32_t dst[K];
+    int idx[K];
+    float w[K];
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        dst[j] = dst_row[(int64_t)t * K + j];
+        idx[j] = topk_idx[(int64_t)t * K + j];
+        w[j] = topk_w[(int64_t)t * K + j];
+        bad |= dst[j] >= n_rows;
+        if (dst[j] >= n_rows) dst[j] = -1;
+    }
+    float acc[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) acc[j] = 0.0f;
+    // the expert rows are read once here: non-temporal loads
+#pragma unroll 2
+    for (int v = lane; v < nvec; v += 64) {
+        const uint4 g = dout[(int64_t)t * nvec + v];
+        uint4 yv[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            if (dst[j] >= 0) {
+                const vu4 q = __builtin_nontemporal_load(reinterpret_cast<const vu4*>(y) + (int64_t)dst[j] * nvec + v);
+                yv[j] = make_uint4(q[0], q[1], q[2], q[3]);
+            }
+        const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            if (dst[j] < 0) continue;
+            const uint32_t yw[4] = {yv[j].x, yv[j].y, yv[j].z, yv[j].w};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                acc[j] = fmaf(bf16_lo(gw[p]), bf16_lo(yw[p]), acc[j]);
+                acc[j] = fmaf(bf16_hi(gw[p]), bf16_hi(yw[p]), acc[j]);
+            }
+            if constexpr (FUSE) dy_perm[(int64_t)dst[j] * nvec + v] = scale_vec<true>(g, w[j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acc[j] += __shfl_xor(acc[j], off, 64);
+    float wdw = 0.0f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) wdw = fmaf(w[j], acc[j], wdw);
+    for (int e = lane; e < E; e += 64) {
+        float v = 0.0f;
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            if (idx[j] == e) v = w[j] * (acc[j] - wdw);
+        dlogits[(int64_t)t * E + e] = v;
+    }
+    if (dw_out) {
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            if (lane == j) dw_out[(int64_t)t * K + j] = acc[j];
+    }
+    if (bad && lane == 0 && dev_err) atomicOr(dev_err, (int)MOE_ERR_ROW_RANGE);
+}
+
 // run f(integral_constant<int, k>) for k in 1..kMaxTopK
 template <class F>
 hipError_t with_k(int k, F&& f)
@@ -488,6 +572,29 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* dst_row,
         });
         if (e != hipSuccess) return e;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_grad(const void* dout, const void* y_perm, const int32_t* topk_idx,
+                            const float* topk_w, const int32_t* dst_row, int T, int E, int k, int d,
+                            int64_t n_rows, float* dlogits, float* dw, void* dy_perm, int32_t* dev_err,
+                            hipStream_t s)
+{
+    if (T == 0) return hipSuccess;
+    const int nvec = d / 8;
+    const unsigned grid = (unsigned)((T + 3) / 4);
+    const hipError_t e = with_k(k, [&](auto kc) {
+        constexpr int K = decltype(kc)::value;
+        if (dy_perm)
+            hipLaunchKernelGGL((gate_grad_kernel<K, true>), dim3(grid), dim3(256), 0, s, (const uint4*)dout,
+                               (const uint4*)y_perm, T, E, nvec, topk_idx, topk_w, dst_row, n_rows, dlogits, dw,
+                               (uint4*)dy_perm, dev_err);
+        else
+            hipLaunchKernelGGL((gate_grad_kernel<K, false>), dim3(grid), dim3(256), 0, s, (const uint4*)dout,
+                               (const uint4*)y_perm, T, E, nvec, topk_idx, topk_w, dst_row, n_rows, dlogits, dw,
+                               (uint4*)nullptr, dev_err);
+    });
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -15,8 +15,9 @@ import torch
 
 from . import (MOE_BF16, MOE_F32, MOE_GEMM_DGRAD_DOWN, MOE_GEMM_DGRAD_GATE_UP, MOE_MXFP8,
                gemm_tensors, moe_gemm_workspace_bytes, moe_grouped_gemm_bwd, moe_grouped_gemm_fwd,
-               moe_grouped_gemm_op, moe_permute, moe_quantize_mxfp8, moe_route_topk,
-               moe_route_workspace_bytes, moe_unpermute_combine)
+               moe_gate_grad, moe_grouped_gemm_op, moe_permute, moe_quantize_mxfp8,
+               moe_route_topk, moe_route_workspace_bytes, moe_router_logits,
+               moe_unpermute_combine)
 
 _ACT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_MXFP8: torch.bfloat16}
 
@@ -149,6 +150,22 @@ class MoELayer:
         w = self.topk_w if weights is None else weights
         moe_unpermute_combine(MOE_F32 if self.dtype == MOE_F32 else MOE_BF16, self.y_perm,
                               self.dst_row, w, self.k, self.out, dev_err=self.dev_err)
+
+    def router_scores(self, x, w_router):
+        """Router scores [T, E] fp32 = x . w_router^T (bf16 x and w_router [E, d])."""
+        if getattr(self, "logits", None) is None:
+            self.logits = torch.empty(self.T, self.E, dtype=torch.float32, device=x.device)
+        moe_router_logits(x, w_router, self.logits)
+        return self.logits
+
+    def gate_grad(self, dout):
+        """dlogits [T, E] fp32: the gradient of <dout, out> through the gate
+        weights of the last forward (bf16 activations; call after forward)."""
+        if getattr(self, "dlogits", None) is None:
+            self.dlogits = torch.empty(self.T, self.E, dtype=torch.float32, device=dout.device)
+        moe_gate_grad(dout, self.y_perm, self.topk_idx, self.topk_w, self.dst_row, self.dlogits,
+                      dev_err=self.dev_err)
+        return self.dlogits
 
     def forward(self, logits, x, weights=None):
         self.route(logits)

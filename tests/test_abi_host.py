@@ -157,6 +157,33 @@ def test_gemm_validation(m):
     assert lib.moe_quantize_mxfp8(P, 10, 64, 1, P, 0, P, P, None) == m.MOE_EINVAL
 
 
+def test_router_and_gate_grad_validation(m):
+    lib = m.load()
+    P = FAKE
+
+    def rl(x=P, w=P, T=100, E=8, d=64, lg=P):
+        return lib.moe_router_logits(x, w, T, E, d, lg, None)
+    assert rl(E=0) == m.MOE_EINVAL
+    assert rl(E=1025) == m.MOE_EINVAL
+    assert rl(T=-1) == m.MOE_EINVAL
+    assert rl(x=None) == m.MOE_EINVAL
+    assert rl(d=12) == m.MOE_EALIGN
+    assert rl(x=P + 8) == m.MOE_EALIGN
+    assert rl(T=0, x=None, w=None, lg=None) == m.MOE_OK     # nothing to do, nothing launched
+
+    def gg(T=100, E=8, k=2, d=64, n_rows=200, dout=P, y=P, dl=P, dyp=None):
+        return lib.moe_gate_grad(dout, y, P, P, P, T, E, k, d, n_rows, dl, None, dyp, None, None)
+    assert gg(k=0) == m.MOE_EINVAL
+    assert gg(k=9) == m.MOE_EINVAL
+    assert gg(E=1, k=2) == m.MOE_EINVAL              # k > E
+    assert gg(dout=None) == m.MOE_EINVAL
+    assert gg(dl=None) == m.MOE_EINVAL
+    assert gg(d=20) == m.MOE_EALIGN
+    assert gg(y=P + 4) == m.MOE_EALIGN
+    assert gg(n_rows=240, dyp=P) == m.MOE_EUNSUPPORTED      # padded layout + fused combine backward
+    assert gg(T=0, n_rows=0, dout=None, y=None, dl=None) == m.MOE_OK
+
+
 def test_gemm_tensors_struct_matches_header(m, tmp_path):
     """The ctypes mirror of moe_gemm_tensors has the C struct's size and offsets."""
     fields = list(m.GEMM_TENSOR_FIELDS) + ["ws_bytes"]
