@@ -716,15 +716,25 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_kernel(KParams p)
 // Router scores: logits [T, E] fp32 = x [T, d] . W_r [E, d]^T, bf16 operands,
 // fp32 accumulate (the gating stays in high precision: tutorial, MXFP8
 // section).  A skinny product (E = 128 at most per tile, K = d): the T x d
-// activations stream from HBM once and set the pace.  A workgroup of 4
-// waves owns 64 rows x 128 experts (each wave 32 x 64), with the x and W_r
+// activations stream from HBM once and set the pace.  A workgroup of 8
+// waves owns 64 rows x 128 experts (each wave 32 x 32; two waves per SIMD,
+// so one computes while the other waits on its loads), with the x and W_r
 // K-steps of 64 moving HBM/L2 -> LDS by direct loads through a 3-stage ring
-// (two K-steps in flight while one is read; a 6-stage ring measured no
-// faster).  The scores leave straight
-// from the accumulators, four consecutive fp32 columns per lane.
-constexpr int kRM = 64, kRN = 128, kRK = 64, kRS = 3;
+// (two K-steps in flight while one is read; 4- and 6-stage rings, 4 waves
+// of 32 x 64, and staggering the workgroups' K order all measured slower).
+// The scores leave straight from the accumulators, four consecutive fp32
+// columns per lane.
+#ifndef MOE_ROUTER_WAVES
+#define MOE_ROUTER_WAVES 8
+#endif
+#ifndef MOE_ROUTER_STAGES
+#define MOE_ROUTER_STAGES 3
+#endif
+constexpr int kRM = 64, kRN = 128, kRK = 64, kRS = MOE_ROUTER_STAGES;
+constexpr int kRW = MOE_ROUTER_WAVES;   // 4: each wave 32 x 64; 8: 32 x 32 (two waves per SIMD)
+constexpr int kRJ = kRW == 8 ? 1 : 2;   // 32-expert blocks per wave
 
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(64 * kRW) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ w, int T, int E,
                                                             int d, float* __restrict__ logits)
 {
@@ -733,7 +743,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
     const int row0 = blockIdx.x * kRM;
     const int n0 = blockIdx.y * kRN;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;   // rows wm*32 .., experts wn*64 ..
+    const int wm = wave / (kRW / 2), wn = wave % (kRW / 2);   // rows wm*32 .., experts wn*32*kRJ ..
     TileSrc sa;
     sa.p0 = x + (int64_t)row0 * d;
     sa.p1 = sa.p0 + (int64_t)(kRM / 2) * d;
@@ -748,11 +758,11 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
     sb.rows0 = max(min(E - n0, kRN / 2), 0);
     sb.rows1 = max(min(E - n0 - kRN / 2, kRN / 2), 0);
     sb.K = d;
-    DirectLoader<kRM, kRK, false, 4> la;
-    DirectLoader<kRN, kRK, false, 4> lb;
+    DirectLoader<kRM, kRK, false, kRW> la;
+    DirectLoader<kRN, kRK, false, kRW> lb;
     la.init(sa);
     lb.init(sb);
-    constexpr int NQ = DirectLoader<kRM, kRK, false, 4>::PER_WAVE + DirectLoader<kRN, kRK, false, 4>::PER_WAVE;
+    constexpr int NQ = DirectLoader<kRM, kRK, false, kRW>::PER_WAVE + DirectLoader<kRN, kRK, false, kRW>::PER_WAVE;
     const int nk = (d + kRK - 1) / kRK;
     auto issue = [&](int kt) __attribute__((always_inline)) {
         uint16_t* st = smem + (kt % kRS) * STAGE;
@@ -760,9 +770,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
         lb.issue(st + kRM * kRK, kt);
     };
     static_assert(kRS >= 2 && kRS <= 6, "the waits below cover up to four later K-steps");
-    f32x16 acc[2];
+    f32x16 acc[kRJ];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kRJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
     for (int kt = 0; kt < kRS - 1 && kt < nk; ++kt) issue(kt);
@@ -784,22 +794,22 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
         for (int ks = 0; ks < kRK / 16; ++ks) {
             const bf16x8 af = read_frag<kRM, kRK, false>(a_s, wm * 32, ks, lane);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const bf16x8 bf = read_frag<kRN, kRK, false>(b_s, wn * 64 + j * 32, ks, lane);
+            for (int j = 0; j < kRJ; ++j) {
+                const bf16x8 bf = read_frag<kRN, kRK, false>(b_s, (wn * kRJ + j) * 32, ks, lane);
                 acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af, acc[j], 0, 0, 0);
             }
         }
     }
     // acc[j] holds the transposed 32 x 32 block (rows wm*32.., experts
-    // wn*64 + 32j ..): lane l has row (l & 31) and, for g = 0..3, the four
-    // experts 8g + 4(l >> 5) + {0..3}
+    // (wn*kRJ + j)*32 ..): lane l has row (l & 31) and, for g = 0..3, the
+    // four experts 8g + 4(l >> 5) + {0..3}
     const int r = row0 + wm * 32 + (lane & 31);
     if (r >= T) return;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kRJ; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const int c = n0 + wn * 64 + j * 32 + 8 * g + 4 * (lane >> 5);
+            const int c = n0 + (wn * kRJ + j) * 32 + 8 * g + 4 * (lane >> 5);
             float* dst = logits + (int64_t)r * E + c;
             if ((E & 3) == 0 && c + 3 < E) {
                 *reinterpret_cast<float4*>(dst) =
@@ -869,7 +879,7 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w, int T, int
 {
     if (T == 0) return hipSuccess;
     const dim3 grid((unsigned)((T + kRM - 1) / kRM), (unsigned)((E + kRN - 1) / kRN));
-    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, s, x, w, T, E, d, logits);
+    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(64 * kRW), 0, s, x, w, T, E, d, logits);
     return hipGetLastError();
 }
 
