@@ -233,7 +233,9 @@ def run_gpu(args, cfg):
     ms_per_step = wall * 1e3 / K
     counts = lay.counts.cpu()
     f1 = router_steps(lay, inp, K) if dt == m.MOE_BF16 and not cap else None
-    return dict(stage_ms=stage_ms, gpu_ms=gpu_ms, ms_per_step=ms_per_step, R=R, cap=cap, f1=f1,
+    f4 = wgrad_f32_accumulate(lay, K) if dt == m.MOE_BF16 and not cap else None
+    wq = weight_requant(lay, K) if dt == m.MOE_MXFP8 else None
+    return dict(stage_ms=stage_ms, gpu_ms=gpu_ms, ms_per_step=ms_per_step, R=R, cap=cap, f1=f1, wq=wq, f4=f4,
                 counts=counts, inp=inp, lay=lay)
 
 
@@ -265,6 +267,55 @@ def router_steps(lay, inp, reps):
         out[name] = {"ms": round(ms, 4), "gbs": round(by / ms / 1e6, 1),
                      "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4), "bytes": by}
     return out
+
+
+def wgrad_f32_accumulate(lay, reps):
+    """The weight-gradient stage adding into fp32 accumulators (the training
+    loop's accumulate-into variant of the bf16 overwrite the step runs),
+    timed alone over `reps` launches after the layer's step.  Bytes: the four
+    activation operands read once and the fp32 accumulators read and written."""
+    import torch
+    E, d, f, R = lay.E, lay.d, lay.f, lay.n_rows
+    a13 = torch.zeros(E, 2 * f, d, dtype=torch.float32, device="cuda")
+    a2 = torch.zeros(E, d, f, dtype=torch.float32, device="cuda")
+    fl = 6 * R * d * f
+    by = R * (2 * d + 3 * f) * 2 + 2 * (a13.numel() + a2.numel()) * 4
+    lay.wgrad_accumulate(a13, a2)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        lay.wgrad_accumulate(a13, a2)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del a13, a2
+    return {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1), "gbs": round(by / ms / 1e6, 1),
+            "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4), "bytes": by, "flops": fl}
+
+
+def weight_requant(lay, reps):
+    """MXFP8: the per-optimizer-step rebuild of the four weight caches (both
+    directions of w13 and w2), timed alone over `reps` rebuilds (not part of
+    the layer step).  Bytes: the bf16 weights read once per direction, codes
+    and scales written."""
+    import torch
+    E, d, f = lay.E, lay.d, lay.f
+    n = E * 3 * f * d                        # weight elements (w13 and w2)
+    by = 2 * n * 2 + int(2 * n * MX_ELEM)    # bf16 read per direction; codes + scales written
+    lay.requantize_weights()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        lay.requantize_weights()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    return {"ms": round(ms, 4), "gbs": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4),
+            "bytes": by}
 
 
 def cpu_baseline(args, cfg, inp):
@@ -409,6 +460,10 @@ def main():
     }
     if res["f1"]:
         out["router_and_gate_grad"] = res["f1"]
+    if res["wq"]:
+        out["mx_weight_requant"] = res["wq"]
+    if res["f4"]:
+        out["wgrad_fp32_accumulate"] = res["f4"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, cfg, res["inp"])
     print(json.dumps(out), flush=True)

@@ -226,6 +226,12 @@ typedef struct moe_gemm_tensors {
     void* dw2;                   /* [E, d, f]                       */
     void* ws;                    /* MOE_MXFP8 workspace             */
     size_t ws_bytes;
+    /* MOE_BF16 WGRAD only, optional (both or neither): fp32 weight-gradient
+     * accumulators [E, 2f, d] and [E, d, f].  When set, WGRAD adds its sums
+     * into them (dw13_f32 += dgu^T x, dw2_f32 += dy^T h, one fp32 addition per
+     * element, no atomics) and does not write dw13 / dw2, which may be NULL. */
+    float* dw13_f32;
+    float* dw2_f32;
 } moe_gemm_tensors;
 
 /*

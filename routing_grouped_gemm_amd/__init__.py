@@ -28,11 +28,13 @@ ABI_FUNCTIONS = ("moe_route_workspace_bytes", "moe_route_topk", "moe_permute",
 
 GEMM_TENSOR_FIELDS = ("x_perm", "x_perm_scales", "w13", "w13_scales", "w2", "w2_scales", "gu",
                       "h", "y_perm", "dy_perm", "dgu", "dx_perm", "dw13", "dw2", "ws")
+GEMM_TENSOR_FIELDS_F32 = ("dw13_f32", "dw2_f32")   # after ws_bytes: fp32 weight-gradient accumulators
 
 
 class MoeGemmTensors(ctypes.Structure):
     """C struct moe_gemm_tensors (device pointers, NULL where unused)."""
-    _fields_ = [(n, ctypes.c_void_p) for n in GEMM_TENSOR_FIELDS] + [("ws_bytes", ctypes.c_size_t)]
+    _fields_ = [(n, ctypes.c_void_p) for n in GEMM_TENSOR_FIELDS] + [("ws_bytes", ctypes.c_size_t)] + \
+        [(n, ctypes.c_void_p) for n in GEMM_TENSOR_FIELDS_F32]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
@@ -188,7 +190,7 @@ def moe_grouped_gemm_bwd(dtype, dy_perm, x_perm, gu, h, w13, w2, group_off, capa
 def gemm_tensors(**tensors):
     """Build a MoeGemmTensors from keyword tensors (names as in GEMM_TENSOR_FIELDS;
     ws is a uint8 workspace tensor whose size becomes ws_bytes)."""
-    bad = set(tensors) - set(GEMM_TENSOR_FIELDS)
+    bad = set(tensors) - set(GEMM_TENSOR_FIELDS) - set(GEMM_TENSOR_FIELDS_F32)
     if bad:
         raise TypeError(f"unknown operand(s) {sorted(bad)}")
     st = MoeGemmTensors(**{n: _p(t) for n, t in tensors.items()})

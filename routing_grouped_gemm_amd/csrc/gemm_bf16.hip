@@ -654,6 +654,7 @@ struct KProblem {
     int mtn, ntn;
     uint16_t* C;           // [E, M, N]
     int64_t ldc, sC;
+    float* Cf;             // if set: [E, M, N] fp32, added into instead of writing C
 };
 
 struct KParams {
@@ -709,8 +710,12 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_kernel(KParams p)
     else
         mainloop<BM, BK, NS, true, true, NW, true>(sa, sb, acc, smem);
 
-    store_tile<BM, NW>(acc, q.C + (int64_t)e * q.sC + (int64_t)mt * BM * q.ldc, q.ldc, q.M - mt * BM, nt * BN,
-                   q.N, reinterpret_cast<uint8_t*>(smem));
+    if (q.Cf)
+        add_tile_f32<BM, NW>(acc, q.Cf + (int64_t)e * q.sC + (int64_t)mt * BM * q.ldc, q.ldc, q.M - mt * BM,
+                             nt * BN, q.N);
+    else
+        store_tile<BM, NW>(acc, q.C + (int64_t)e * q.sC + (int64_t)mt * BM * q.ldc, q.ldc, q.M - mt * BM,
+                           nt * BN, q.N, reinterpret_cast<uint8_t*>(smem));
 }
 
 // Router scores: logits [T, E] fp32 = x [T, d] . W_r [E, d]^T, bf16 operands,
@@ -962,6 +967,7 @@ hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, i
         a.mtn = (d + kBMK - 1) / kBMK;
         a.ntn = (f + BN - 1) / BN;
         a.C = (uint16_t*)t.dw2;
+        a.Cf = t.dw2_f32;
         a.ldc = f;
         a.sC = (int64_t)d * f;
         KProblem& b = k.pr[1];
@@ -974,6 +980,7 @@ hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, i
         b.mtn = (2 * f + kBMK - 1) / kBMK;
         b.ntn = (d + BN - 1) / BN;
         b.C = (uint16_t*)t.dw13;
+        b.Cf = t.dw13_f32;
         b.ldc = d;
         b.sC = (int64_t)2 * f * d;
         return launch_k<kBMK, kBK, kNS, kNW>(k, s);

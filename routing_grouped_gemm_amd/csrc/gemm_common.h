@@ -544,6 +544,48 @@ __device__ __forceinline__ void grouped_tile(int local, int mtn, int ntn, int GM
     nt = r / gm;
 }
 
+// add a BM x 256 accumulator tile into fp32 rows of C (rows [0, rows),
+// columns col0 + [0, 256) below N; N % 4 == 0, C 16-byte aligned) straight
+// from the accumulator layout: each lane reads, adds and writes back its
+// four consecutive columns of one row, 32 rows at a time (all of a 32-row
+// block's reads before its writes).  Staging the fp32 tile through the LDS
+// for whole-row accesses measured no faster: the read-modify-write of the
+// tile is bound by the HBM traffic of the tiles finishing together.
+template <int BM, int NW>
+__device__ __forceinline__ void add_tile_f32(const f32x16 (&acc)[BM / 64][WL<NW>::NJ], float* C, int64_t ldc,
+                                             int rows, int col0, int N)
+{
+    constexpr int NJ = WL<NW>::NJ;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = WL<NW>::wm(wave), wn = WL<NW>::wn(wave);
+#pragma unroll
+    for (int i = 0; i < BM / 64; ++i) {
+        const int r = wm * (BM / 2) + i * 32 + (lane & 31);
+        float4 v[NJ][4];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c = col0 + acc_col<NW>(wn, j, g, lane);
+                if (r < rows && c < N) v[j][g] = *reinterpret_cast<const float4*>(C + r * ldc + c);
+            }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int c = col0 + acc_col<NW>(wn, j, g, lane);
+                if (r < rows && c < N) {
+                    float4 o = v[j][g];
+                    o.x += acc[i][j][4 * g];
+                    o.y += acc[i][j][4 * g + 1];
+                    o.z += acc[i][j][4 * g + 2];
+                    o.w += acc[i][j][4 * g + 3];
+                    *reinterpret_cast<float4*>(C + r * ldc + c) = o;
+                }
+            }
+    }
+}
+
 // store a BM x 256 accumulator tile as bf16 rows of C (rows [0, rows), columns
 // col0 + [0, 256) below N), through the LDS staging above
 template <int BM, int NW = 4>

@@ -249,8 +249,16 @@ int moe_grouped_gemm_op(int op, int dtype, const moe_gemm_tensors* t,
     case MOE_GEMM_DGRAD_GATE_UP: need[0] = t->dgu; need[1] = t->w13; need[2] = t->dx_perm; n = 3; break;
     default: break;
     }
+    const bool acc_f32 = t->dw13_f32 || t->dw2_f32;
+    if (acc_f32) {
+        // fp32 accumulate-into weight gradients: bf16 WGRAD only, both targets
+        if (op != MOE_GEMM_WGRAD || dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+        if (!t->dw13_f32 || !t->dw2_f32) return MOE_EINVAL;
+        if (!aligned16(t->dw13_f32) || !aligned16(t->dw2_f32)) return MOE_EALIGN;
+    }
     if (op == MOE_GEMM_WGRAD) {
-        const void* wn[6] = {t->dy_perm, t->h, t->dw2, t->dgu, t->x_perm, t->dw13};
+        const void* wn[6] = {t->dy_perm, t->h, acc_f32 ? (const void*)t->dw2_f32 : t->dw2, t->dgu, t->x_perm,
+                             acc_f32 ? (const void*)t->dw13_f32 : t->dw13};
         for (const void* p : wn) {
             if (!p) return MOE_EINVAL;
             if (!aligned16(p)) return MOE_EALIGN;

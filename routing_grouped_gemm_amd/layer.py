@@ -13,7 +13,8 @@ The backward of the layer with the routing held fixed:
 """
 import torch
 
-from . import (MOE_BF16, MOE_F32, MOE_GEMM_DGRAD_DOWN, MOE_GEMM_DGRAD_GATE_UP, MOE_MXFP8,
+from . import (MOE_BF16, MOE_F32, MOE_GEMM_DGRAD_DOWN, MOE_GEMM_DGRAD_GATE_UP, MOE_GEMM_WGRAD,
+               MOE_MXFP8,
                gemm_tensors, moe_gemm_workspace_bytes, moe_grouped_gemm_bwd, moe_grouped_gemm_fwd,
                moe_gate_grad, moe_grouped_gemm_op, moe_permute, moe_quantize_mxfp8,
                moe_route_topk, moe_route_workspace_bytes, moe_router_logits,
@@ -83,22 +84,28 @@ class MoELayer:
         # forward direction: blocks along the contraction dim of each GEMM
         self.w13_q = torch.empty(E * 2 * f, d, **u8)
         self.w13_s = torch.empty(E * 2 * f, d // 32, **u8)
-        moe_quantize_mxfp8(w13.reshape(E * 2 * f, d), 0, self.w13_q, self.w13_s)
         self.w2_q = torch.empty(E * d, f, **u8)
         self.w2_s = torch.empty(E * d, f // 32, **u8)
-        moe_quantize_mxfp8(w2.reshape(E * d, f), 0, self.w2_q, self.w2_s)
         # backward direction: each expert's matrix transposed, blocks along 2f / d
         # (column-wise quantiser layout: K * (rows + 128 * groups) codes)
-        g13 = torch.arange(0, E + 1, dtype=torch.int32, device=dev) * (2 * f)
-        g2 = torch.arange(0, E + 1, dtype=torch.int32, device=dev) * d
+        self._g13 = torch.arange(0, E + 1, dtype=torch.int32, device=dev) * (2 * f)
+        self._g2 = torch.arange(0, E + 1, dtype=torch.int32, device=dev) * d
         n13 = d * (E * 2 * f + 128 * E)
         n2 = f * (E * d + 128 * E)
         self.w13t_q = torch.empty(n13, **u8)
         self.w13t_s = torch.empty(n13 // 32, **u8)
-        moe_quantize_mxfp8(w13.reshape(E * 2 * f, d), 1, self.w13t_q, self.w13t_s, g13, E)
         self.w2t_q = torch.empty(n2, **u8)
         self.w2t_s = torch.empty(n2 // 32, **u8)
-        moe_quantize_mxfp8(w2.reshape(E * d, f), 1, self.w2t_q, self.w2t_s, g2, E)
+        self.requantize_weights()
+
+    def requantize_weights(self):
+        """MXFP8: rebuild the four weight caches (forward and backward direction
+        of w13 and w2) from the bf16 weights in place, as an optimizer step does."""
+        E, f, d = self.E, self.f, self.d
+        moe_quantize_mxfp8(self.w13.reshape(E * 2 * f, d), 0, self.w13_q, self.w13_s)
+        moe_quantize_mxfp8(self.w2.reshape(E * d, f), 0, self.w2_q, self.w2_s)
+        moe_quantize_mxfp8(self.w13.reshape(E * 2 * f, d), 1, self.w13t_q, self.w13t_s, self._g13, E)
+        moe_quantize_mxfp8(self.w2.reshape(E * d, f), 1, self.w2t_q, self.w2t_s, self._g2, E)
 
     # -------------------------------------------------------------- stages
     def _stage_tensors(self):
@@ -126,6 +133,16 @@ class MoELayer:
         bwd = op in (MOE_GEMM_DGRAD_DOWN, MOE_GEMM_DGRAD_GATE_UP)
         moe_grouped_gemm_op(op, self.dtype, self._stages[1 if bwd else 0], self.offsets,
                             self.capacity, self.E, self.n_rows, self.d, self.f)
+
+    def wgrad_accumulate(self, dw13_f32, dw2_f32):
+        """bf16: the weight-gradient stage adding into fp32 accumulators
+        (dw13_f32 += dgu^T x_perm, dw2_f32 += dy_perm^T h, per expert) instead
+        of writing the bf16 dw13 / dw2.  Call after backward (it reads dgu)."""
+        self._alloc_bwd()
+        t = gemm_tensors(x_perm=self.x_perm, h=self.h, dy_perm=self.dy_perm, dgu=self.dgu,
+                         dw13_f32=dw13_f32, dw2_f32=dw2_f32)
+        moe_grouped_gemm_op(MOE_GEMM_WGRAD, self.dtype, t, self.offsets, self.capacity, self.E,
+                            self.n_rows, self.d, self.f)
 
     # -------------------------------------------------------------- steps
     def route(self, logits):

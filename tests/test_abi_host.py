@@ -184,9 +184,27 @@ def test_router_and_gate_grad_validation(m):
     assert gg(T=0, n_rows=0, dout=None, y=None, dl=None) == m.MOE_OK
 
 
+def test_wgrad_fp32_accumulate_validation(m):
+    lib = m.load()
+    P = FAKE
+    t = m.MoeGemmTensors(**{n: P for n in m.GEMM_TENSOR_FIELDS})
+
+    def op(o, dtype=m.MOE_BF16, t=t):
+        return lib.moe_grouped_gemm_op(o, dtype, ctypes.byref(t), P, 0, 8, 0, 128, 128, None)
+    t.dw13_f32, t.dw2_f32 = P, None
+    assert op(m.MOE_GEMM_WGRAD) == m.MOE_EINVAL               # both accumulators or neither
+    t.dw2_f32 = P + 8
+    assert op(m.MOE_GEMM_WGRAD) == m.MOE_EALIGN
+    t.dw2_f32 = P
+    assert op(m.MOE_GEMM_DGRAD_GATE_UP) == m.MOE_EUNSUPPORTED  # accumulate-into is a WGRAD option
+    assert op(m.MOE_GEMM_WGRAD, dtype=m.MOE_F32) == m.MOE_EUNSUPPORTED
+    t.dw13_f32, t.dw2_f32, t.dy_perm = P, P, None
+    assert op(m.MOE_GEMM_WGRAD) == m.MOE_EINVAL               # operands still required
+
+
 def test_gemm_tensors_struct_matches_header(m, tmp_path):
     """The ctypes mirror of moe_gemm_tensors has the C struct's size and offsets."""
-    fields = list(m.GEMM_TENSOR_FIELDS) + ["ws_bytes"]
+    fields = list(m.GEMM_TENSOR_FIELDS) + ["ws_bytes"] + list(m.GEMM_TENSOR_FIELDS_F32)
     src = tmp_path / "layout.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\nint main(void){\n'
                    '  printf("%zu\\n", sizeof(moe_gemm_tensors));\n'

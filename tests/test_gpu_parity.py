@@ -170,6 +170,35 @@ def test_layer_fwd_bwd_parity(moe, T, d, E, f, k, dtype, C):
         assert torch.all(lay.dw13[E - 2] == 0) and torch.all(lay.dw2[E - 2] == 0)
 
 
+@pytest.mark.parametrize("T,d,E,f,k,C", [(384, 256, 5, 384, 2, 0), (400, 128, 8, 128, 2, 70),
+                                         (1100, 256, 4, 256, 1, 0)])
+def test_wgrad_fp32_accumulate(moe, T, d, E, f, k, C):
+    # the weight-gradient stage adding into fp32 accumulators: twice onto a
+    # random start, each addition against the oracle's weight gradient
+    _say("wgrad-f32-accumulate", T, d, E, f, k, C)
+    inp = moe_synth.make_inputs(T=T, d=d, E=E, f=f, k=k, seed=T + 3 * d)
+    if E > 2:
+        inp["logits"][:, E - 2] -= 1e30            # one expert gets no rows
+    lay = _run_layer(moe, inp, k, "bf16", C)
+    ref = oracle_layer(inp, k, capacity=C, round_mode=oracle.BF16)
+    a13 = moe_synth.normal((E, 2 * f, d), 1e-3, 5, DEV)
+    a2 = moe_synth.normal((E, d, f), 1e-3, 6, DEV)
+    s13, s2 = a13.clone(), a2.clone()
+    lay.wgrad_accumulate(a13, a2)
+    torch.cuda.synchronize()
+    one13, one2 = a13.clone(), a2.clone()
+    lay.wgrad_accumulate(a13, a2)
+    torch.cuda.synchronize()
+    assert_close(np64(one13 - s13), ref["dw13"], BF16_TOL, "dw13 += (first)")
+    assert_close(np64(one2 - s2), ref["dw2"], BF16_TOL, "dw2 += (first)")
+    assert_close(np64(a13 - one13), ref["dw13"], BF16_TOL, "dw13 += (second)")
+    assert_close(np64(a2 - one2), ref["dw2"], BF16_TOL, "dw2 += (second)")
+    if E > 2:   # an expert with no rows adds exactly nothing
+        assert torch.equal(a13[E - 2], s13[E - 2]) and torch.equal(a2[E - 2], s2[E - 2])
+    # the bf16 gradients of the same backward are untouched
+    assert_close(np64(lay.dw13), ref["dw13"], BF16_TOL, "dw13")
+
+
 def test_layer_deterministic(moe):
     _say("layer-determinism")
     inp = moe_synth.make_inputs(T=384, d=256, E=5, f=384, k=2, seed=5)
