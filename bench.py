@@ -176,14 +176,15 @@ def run_gpu(args, cfg):
     if args.padded:
         cap = moe_synth.capacity_of(T, k, E, cfg.get("capacity_factor", 1.25))
     inp = moe_synth.make_inputs(args.workload, device="cuda")
-    lay = MoELayer(T, d, E, f, k, dt, capacity=cap)
+    S = cfg.get("n_shared", 0)
+    lay = MoELayer(T, d, E, f, k, dt, capacity=cap, n_shared=S)
     lay.set_weights(inp["w13"], inp["w2"])
     lay._alloc_bwd()
     R = lay.n_rows
     act_dt = m.MOE_F32 if dt == m.MOE_F32 else m.MOE_BF16
     # combine weights: the router's softmax weights, or the per-row gate a
     # received expert-parallel shard comes with
-    wts = inp["gate"] if "gate" in inp else lay.topk_w
+    wts = inp["gate"] if "gate" in inp else lay.s_w
 
     def step(ev):
         def mark(i):
@@ -200,7 +201,7 @@ def run_gpu(args, cfg):
         mark(4)
         lay.combine(wts)
         mark(5)
-        m.moe_permute(act_dt, inp["dout"], k, lay.dst_row, lay.dy_perm, src_slot=lay.src_slot,
+        m.moe_permute(act_dt, inp["dout"], lay.K, lay.s_dst, lay.dy_perm, src_slot=lay.s_src,
                       row_scale=wts, dev_err=lay.dev_err)
         mark(6)
         lay.gemm_stage(m.MOE_GEMM_DGRAD_DOWN)
@@ -209,7 +210,7 @@ def run_gpu(args, cfg):
         mark(8)
         lay.gemm_stage(m.MOE_GEMM_WGRAD)
         mark(9)
-        m.moe_unpermute_combine(act_dt, lay.dx_perm, lay.dst_row, None, k, lay.dx,
+        m.moe_unpermute_combine(act_dt, lay.dx_perm, lay.s_dst, None, lay.K, lay.dx,
                                 dev_err=lay.dev_err)
         mark(10)
 
@@ -276,8 +277,8 @@ def wgrad_f32_accumulate(lay, reps):
     activation operands read once and the fp32 accumulators read and written."""
     import torch
     E, d, f, R = lay.E, lay.d, lay.f, lay.n_rows
-    a13 = torch.zeros(E, 2 * f, d, dtype=torch.float32, device="cuda")
-    a2 = torch.zeros(E, d, f, dtype=torch.float32, device="cuda")
+    a13 = torch.zeros(lay.G, 2 * f, d, dtype=torch.float32, device="cuda")
+    a2 = torch.zeros(lay.G, d, f, dtype=torch.float32, device="cuda")
     fl = 6 * R * d * f
     by = R * (2 * d + 3 * f) * 2 + 2 * (a13.numel() + a2.numel()) * 4
     lay.wgrad_accumulate(a13, a2)
@@ -376,11 +377,13 @@ def cpu_baseline(args, cfg, inp):
                             round_mode=oracle.BF16)
         oracle.ffn_bwd(dy, x, gu, h, w13, w2, go, oracle.BF16)
     t_ffn = time.perf_counter() - t1
+    # shared experts run the same per-row FFN over T more rows each
+    rows_total += cfg.get("n_shared", 0) * T
     t_full = t_route + t_ffn * rows_total / max(rows, 1)
     return {"value": T / t_full, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": (f"oracle route over all {T} tokens ({t_route:.2f} s) + expert FFN fwd+bwd "
                        f"for the first {rows} rows of experts 0..{n_exp - 1} ({t_ffn:.2f} s), "
-                       f"scaled to all {rows_total} routed rows"),
+                       f"scaled to all {rows_total} expert rows"),
             "sample_seconds": round(t_route + t_ffn, 2)}
 
 
@@ -414,10 +417,13 @@ def main():
     R = res["R"]
     mx = cfg["dtype"] == "mxfp8"
     elem = 4 if cfg["dtype"] == "f32" else 2
-    routed = T * k - (0 if not args.padded else int((res["lay"].dst_row < 0).sum().item()))
+    # shared experts: extra groups of T rows each, extra slots per token
+    S = cfg.get("n_shared", 0)
+    routed = T * k - (0 if not args.padded else int((res["lay"].dst_row < 0).sum().item())) + S * T
+    Eg, kg = E + S, k + S   # GEMM groups and slots per token
     stages = {}
     for s in STAGES:
-        fl, by = stage_work(s, T, d, E, f, k, routed, elem, mx)
+        fl, by = stage_work(s, T, d, Eg, f, kg, routed, elem, mx)
         ms = res["stage_ms"][s]
         ent = {"ms": round(ms, 4)}
         if fl:
@@ -429,7 +435,7 @@ def main():
     gemm_flops = 18 * routed * d * f
     peak = PEAK_FP8_TFLOPS if mx else (PEAK_BF16_TFLOPS if elem == 2 else PEAK_F32_TFLOPS)
     dom = max(STAGES, key=lambda s: res["stage_ms"][s])
-    fl, by = stage_work(dom, T, d, E, f, k, routed, elem, mx)
+    fl, by = stage_work(dom, T, d, Eg, f, kg, routed, elem, mx)
     dom_ms = res["stage_ms"][dom]
     if fl:
         rl = {"bound": "alu" if elem == 4 else "mfma", "achieved": round(fl / dom_ms / 1e9, 1),
@@ -449,9 +455,11 @@ def main():
         "dtype": cfg["dtype"], "data": "synthetic",
         "config": {"workload": (f"{args.workload}: T={T} d_model={d} E={E} d_ff={f} top-{k} "
                                 f"{cfg['dtype']} SwiGLU, {cfg['routing']} routing, fwd+bwd"
-                                + (" padded C=%d" % res["cap"] if args.padded else "")),
+                                + (" padded C=%d" % res["cap"] if args.padded else "")
+                                + (f", {S} shared expert(s)" if S else "")),
                    "tokens": T, "experts": E, "top_k": k, "d_model": d, "d_ff": f,
-                   "routed_rows": routed, "executed_rows": R, "seed": moe_synth.seed_of(args.workload)},
+                   "routed_rows": routed, "executed_rows": R, "shared_experts": S,
+                   "seed": moe_synth.seed_of(args.workload)},
         "gemm": {"ms": round(gemm_ms, 4), "tflops": round(gemm_flops / gemm_ms / 1e9, 1),
                  "frac_peak": round(gemm_flops / gemm_ms / 1e9 / peak, 4)},
         "stages": stages, "gpu_event_ms_per_step": round(res["gpu_ms"], 4),

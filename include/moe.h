@@ -285,6 +285,32 @@ MOE_API int moe_quantize_mxfp8(const void* src, int64_t rows, int K, int colwise
                        uint8_t* scales, moe_stream_t stream);
 
 /*
+ * Shared experts (ungated experts every token also uses; several of them
+ * equal one wider expert) as extra groups of the same grouped GEMM: from a
+ * route of k slots, the route of k + n_shared slots in which slot k + s of
+ * token t is expert E + s with weight 1 and row R + s*T + t, after the R
+ * routed rows (R = T*k, or E*C padded).  Then permute, the grouped GEMM
+ * (E + n_shared groups; weights of the shared experts after the routed
+ * ones; group offsets = offsets_out, capacity 0) and combine run unchanged
+ * on the wider route.
+ * in   the route of moe_route_topk: topk_idx, topk_w, dst_row [T, k],
+ *      counts [E], offsets [E+1], src_slot [n_rows]; capacity as given there.
+ * out  topk_idx_out, topk_w_out, dst_row_out [T, k + n_shared];
+ *      counts_out [E + n_shared]; offsets_out [E + n_shared + 1] (group
+ *      starts: the routed offsets, or e*C when padded, then R + s*T);
+ *      src_slot_out [n_rows + n_shared*T], routed rows renumbered to
+ *      t*(k + n_shared) + j, padding rows -1.
+ * Errors: MOE_EINVAL (sizes: n_shared >= 1, k + n_shared <= 8,
+ * E + n_shared <= 1024, n_rows as the route; null pointers).
+ */
+MOE_API int moe_route_add_shared(int T, int E, int k, int n_shared, int capacity,
+                                 const int32_t* topk_idx, const float* topk_w, const int32_t* dst_row,
+                                 const int32_t* counts, const int32_t* offsets, const int32_t* src_slot,
+                                 int64_t n_rows, int32_t* topk_idx_out, float* topk_w_out,
+                                 int32_t* counts_out, int32_t* offsets_out, int32_t* dst_row_out,
+                                 int32_t* src_slot_out, moe_stream_t stream);
+
+/*
  * Router scores, the step before moe_route_topk:
  *   logits[t, e] = sum_i x[t, i] * w_router[e, i]
  * bf16 operands, fp32 accumulation and fp32 result (the tutorial's MXFP8

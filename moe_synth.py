@@ -33,6 +33,9 @@ WORKLOADS = {
                      routing="uniform", bwd=True, gate="uniform01"),
     "e8_matched": dict(idx=5, T=16384, d=4096, E=8, f=1536, k=4, dtype="bf16",
                        routing="uniform", bwd=True),
+    # e128 plus one shared expert (ungated, every token) of the same width
+    "e128_shared": dict(idx=6, T=16384, d=4096, E=128, f=1536, k=4, n_shared=1, dtype="bf16",
+                        routing="uniform", bwd=True),
 }
 
 ZIPF_S = 1.2
@@ -98,8 +101,9 @@ def make_inputs(name=None, device="cpu", seed=None, act_dtype=None, **over):
     out = dict(cfg=cfg, seed=seed)
     out["logits"] = router_logits(T, E, s + 1, cfg["routing"], device)
     out["x"] = normal((T, d), 0.02, s + 2, device, act_dtype)
-    out["w13"] = normal((E, 2 * f, d), 0.02, s + 3, device, act_dtype)
-    out["w2"] = normal((E, d, f), 0.02, s + 4, device, act_dtype)
+    Ew = E + cfg.get("n_shared", 0)   # expert weights: the routed ones, then the shared ones
+    out["w13"] = normal((Ew, 2 * f, d), 0.02, s + 3, device, act_dtype)
+    out["w2"] = normal((Ew, d, f), 0.02, s + 4, device, act_dtype)
     out["dout"] = normal((T, d), 1.0, s + 5, device, act_dtype)
     # router weights [E, d]: std 1 / (0.02 sqrt(d)), so that with x ~ N(0, 0.02)
     # the router scores x . W_r^T are about N(0, 1) like the logits above

@@ -24,7 +24,8 @@ MOE_GEMM_GATE_UP, MOE_GEMM_DOWN, MOE_GEMM_DGRAD_DOWN, MOE_GEMM_DGRAD_GATE_UP, MO
 ABI_FUNCTIONS = ("moe_route_workspace_bytes", "moe_route_topk", "moe_permute",
                  "moe_gemm_workspace_bytes", "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd",
                  "moe_grouped_gemm_op", "moe_unpermute_combine", "moe_quantize_mxfp8",
-                 "moe_router_logits", "moe_gate_grad", "moe_status_string", "moe_version")
+                 "moe_route_add_shared", "moe_router_logits", "moe_gate_grad", "moe_status_string",
+                 "moe_version")
 
 GEMM_TENSOR_FIELDS = ("x_perm", "x_perm_scales", "w13", "w13_scales", "w2", "w2_scales", "gu",
                       "h", "y_perm", "dy_perm", "dgu", "dx_perm", "dw13", "dw2", "ws")
@@ -82,6 +83,8 @@ def load():
     lib.moe_unpermute_combine.argtypes = [I, P, P, P, I, I, I, I64, P, P, P]
     lib.moe_quantize_mxfp8.restype = I
     lib.moe_quantize_mxfp8.argtypes = [P, I64, I, I, P, I, P, P, P]
+    lib.moe_route_add_shared.restype = I
+    lib.moe_route_add_shared.argtypes = [I, I, I, I, I, P, P, P, P, P, P, I64, P, P, P, P, P, P, P]
     lib.moe_router_logits.restype = I
     lib.moe_router_logits.argtypes = [P, P, I, I, I, P, P]
     lib.moe_gate_grad.restype = I
@@ -213,6 +216,19 @@ def moe_unpermute_combine(dtype, y_perm, dst_row, weights, k, out, dev_err=None,
     rc = load().moe_unpermute_combine(dtype, _p(y_perm), _p(dst_row), _p(weights), T, k, d,
                                       n_rows, _p(out), _p(dev_err), _s(stream))
     _check(rc, "moe_unpermute_combine")
+
+
+def moe_route_add_shared(n_shared, capacity, topk_idx, topk_w, dst_row, counts, offsets, src_slot,
+                         topk_idx_out, topk_w_out, counts_out, offsets_out, dst_row_out, src_slot_out,
+                         stream=None):
+    """The route of k slots -> the route of k + n_shared slots (shared experts E .. E+n_shared-1)."""
+    T, k = topk_idx.shape
+    E = counts.numel()
+    rc = load().moe_route_add_shared(T, E, k, n_shared, capacity, _p(topk_idx), _p(topk_w), _p(dst_row),
+                                     _p(counts), _p(offsets), _p(src_slot), src_slot.numel(), _p(topk_idx_out),
+                                     _p(topk_w_out), _p(counts_out), _p(offsets_out), _p(dst_row_out),
+                                     _p(src_slot_out), _s(stream))
+    _check(rc, "moe_route_add_shared")
 
 
 def moe_router_logits(x, w_router, logits, stream=None):

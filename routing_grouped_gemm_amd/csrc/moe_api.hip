@@ -96,6 +96,28 @@ int moe_route_topk(const float* logits, int T, int E, int k, int capacity, int32
                                   as_stream(stream)));
 }
 
+int moe_route_add_shared(int T, int E, int k, int n_shared, int capacity, const int32_t* topk_idx,
+                         const float* topk_w, const int32_t* dst_row, const int32_t* counts,
+                         const int32_t* offsets, const int32_t* src_slot, int64_t n_rows,
+                         int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                         int32_t* offsets_out, int32_t* dst_row_out, int32_t* src_slot_out,
+                         moe_stream_t stream)
+{
+    if (T < 0 || E < 1 || k < 1 || n_shared < 1 || k + n_shared > kMaxTopK || E + n_shared > kMaxExperts ||
+        capacity < 0)
+        return MOE_EINVAL;
+    const int64_t want_rows = capacity > 0 ? (int64_t)E * capacity : (int64_t)T * k;
+    if (n_rows != want_rows || n_rows + (int64_t)n_shared * T >= kMaxRows) return MOE_EINVAL;
+    if (!counts || !offsets || !counts_out || !offsets_out) return MOE_EINVAL;
+    if (T > 0 && (!topk_idx || !topk_w || !dst_row || !topk_idx_out || !topk_w_out || !dst_row_out ||
+                  !src_slot_out))
+        return MOE_EINVAL;
+    if (n_rows > 0 && !src_slot) return MOE_EINVAL;
+    return status_of(launch_route_add_shared(topk_idx, topk_w, dst_row, counts, offsets, src_slot, T, E, k,
+                                             n_shared, capacity, n_rows, topk_idx_out, topk_w_out, counts_out,
+                                             offsets_out, dst_row_out, src_slot_out, as_stream(stream)));
+}
+
 int moe_permute(int dtype, const void* x, int T, int d, int k, const int32_t* dst_row,
                 const int32_t* src_slot, const float* row_scale, int64_t n_rows, void* x_perm,
                 uint8_t* x_perm_scales, int32_t* dev_err, moe_stream_t stream)

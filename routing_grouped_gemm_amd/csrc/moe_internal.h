@@ -143,6 +143,11 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int capacity, 
                         float* topk_w, int32_t* counts, int32_t* offsets, int32_t* dst_row,
                         int32_t* src_slot, int64_t n_rows, int32_t* lrank, int32_t* hist,
                         int32_t* dev_err, hipStream_t stream);
+hipError_t launch_route_add_shared(const int32_t* idx_in, const float* w_in, const int32_t* dst_in,
+                                   const int32_t* counts_in, const int32_t* offsets_in,
+                                   const int32_t* src_in, int T, int E, int k, int S, int capacity,
+                                   int64_t R, int32_t* idx_out, float* w_out, int32_t* counts_out,
+                                   int32_t* offsets_out, int32_t* dst_out, int32_t* src_out, hipStream_t s);
 // permute / combine / quantise
 hipError_t launch_permute(int dtype, const void* x, int T, int d, int k, const int32_t* dst_row,
                           const int32_t* src_slot, const float* row_scale, int64_t n_rows,

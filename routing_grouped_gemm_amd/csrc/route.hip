@@ -16,6 +16,8 @@
 //      counts, and the exclusive scan of counts (-> offsets).
 //   3. route_finalize_kernel: dst_row = offsets[e] + base + local rank (or
 //      the padded row), src_slot as its inverse, padding rows -1.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -274,7 +276,68 @@ void launch_topk(int nblk, hipStream_t s, const float* logits, int T, int E, int
                        k, nblk, topk_idx, topk_w, lrank, hist, dev_err);
 }
 
+// Shared experts as extra groups: every token also takes slots k .. k+S-1,
+// expert E + s with weight 1, whose rows follow the routed rows expert by
+// expert (row R + s*T + t).  Copies the routed slots into the wider [T, k+S]
+// arrays, renumbers the routed rows' source slots (t*k + j -> t*(k+S) + j),
+// and extends counts and offsets (offsets become the group starts also in
+// the padded layout: e*C for the routed experts).
+__global__ __launch_bounds__(256) void route_add_shared_kernel(
+    const int32_t* __restrict__ idx_in, const float* __restrict__ w_in, const int32_t* __restrict__ dst_in,
+    const int32_t* __restrict__ counts_in, const int32_t* __restrict__ offsets_in,
+    const int32_t* __restrict__ src_in, int T, int E, int k, int S, int capacity, int64_t R,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ counts_out,
+    int32_t* __restrict__ offsets_out, int32_t* __restrict__ dst_out, int32_t* __restrict__ src_out)
+{
+    const int KS = k + S;
+    const int64_t n_slots = (int64_t)T * KS;
+    const int64_t n_rows = R + (int64_t)S * T;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_slots; i += stride) {
+        const int64_t t = i / KS;
+        const int j = (int)(i - t * KS);
+        if (j < k) {
+            idx_out[i] = idx_in[t * k + j];
+            w_out[i] = w_in[t * k + j];
+            dst_out[i] = dst_in[t * k + j];
+        } else {
+            idx_out[i] = E + (j - k);
+            w_out[i] = 1.0f;
+            dst_out[i] = (int32_t)(R + (int64_t)(j - k) * T + t);
+        }
+    }
+    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < n_rows; r += stride) {
+        if (r < R) {
+            const int32_t p = src_in[r];
+            src_out[r] = p < 0 ? -1 : (int32_t)((p / k) * KS + p % k);
+        } else {
+            const int64_t q = r - R;
+            const int64_t t = q % T;
+            src_out[r] = (int32_t)(t * KS + k + q / T);
+        }
+    }
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e <= E + S; e += stride) {
+        if (e < E + S) counts_out[e] = e < E ? counts_in[e] : T;
+        offsets_out[e] = e <= E ? (capacity > 0 ? (int32_t)(e * capacity) : offsets_in[e])
+                                : (int32_t)(R + (e - E) * (int64_t)T);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_route_add_shared(const int32_t* idx_in, const float* w_in, const int32_t* dst_in,
+                                   const int32_t* counts_in, const int32_t* offsets_in,
+                                   const int32_t* src_in, int T, int E, int k, int S, int capacity,
+                                   int64_t R, int32_t* idx_out, float* w_out, int32_t* counts_out,
+                                   int32_t* offsets_out, int32_t* dst_out, int32_t* src_out, hipStream_t s)
+{
+    const int64_t n = std::max<int64_t>({(int64_t)T * (k + S), R + (int64_t)S * T, (int64_t)E + S + 1});
+    const int64_t grid = std::min<int64_t>((n + 255) / 256, 65535);
+    hipLaunchKernelGGL(route_add_shared_kernel, dim3((unsigned)grid), dim3(256), 0, s, idx_in, w_in, dst_in,
+                       counts_in, offsets_in, src_in, T, E, k, S, capacity, R, idx_out, w_out, counts_out,
+                       offsets_out, dst_out, src_out);
+    return hipGetLastError();
+}
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int capacity, int32_t* topk_idx,
                         float* topk_w, int32_t* counts, int32_t* offsets, int32_t* dst_row,

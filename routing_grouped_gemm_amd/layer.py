@@ -17,17 +17,26 @@ from . import (MOE_BF16, MOE_F32, MOE_GEMM_DGRAD_DOWN, MOE_GEMM_DGRAD_GATE_UP, M
                MOE_MXFP8,
                gemm_tensors, moe_gemm_workspace_bytes, moe_grouped_gemm_bwd, moe_grouped_gemm_fwd,
                moe_gate_grad, moe_grouped_gemm_op, moe_permute, moe_quantize_mxfp8,
-               moe_route_topk, moe_route_workspace_bytes, moe_router_logits,
+               moe_route_add_shared, moe_route_topk, moe_route_workspace_bytes, moe_router_logits,
                moe_unpermute_combine)
 
 _ACT = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_MXFP8: torch.bfloat16}
 
 
 class MoELayer:
-    def __init__(self, T, d, E, f, k, dtype=MOE_BF16, capacity=0, device="cuda"):
+    """n_shared > 0 adds that many shared experts (ungated, every token, weight
+    1) as extra groups E .. E+n_shared-1 of the same grouped GEMM: weights are
+    then [E + n_shared, ...] with the shared experts last, and the buffers hold
+    the routed rows followed by n_shared * T shared rows."""
+
+    def __init__(self, T, d, E, f, k, dtype=MOE_BF16, capacity=0, device="cuda", n_shared=0):
         self.T, self.d, self.E, self.f, self.k = T, d, E, f, k
         self.dtype, self.capacity, self.device = dtype, capacity, device
-        self.n_rows = E * capacity if capacity > 0 else T * k
+        self.S = n_shared
+        self.K = k + n_shared                  # slots per token (routed, then shared)
+        self.G = E + n_shared                  # GEMM groups
+        self.R = E * capacity if capacity > 0 else T * k   # routed rows
+        self.n_rows = self.R + n_shared * T
         R = self.n_rows
         act = _ACT[dtype]
         i32 = dict(dtype=torch.int32, device=device)
@@ -36,7 +45,20 @@ class MoELayer:
         self.counts = torch.empty(E, **i32)
         self.offsets = torch.empty(E + 1, **i32)
         self.dst_row = torch.empty(T * k, **i32)
-        self.src_slot = torch.empty(R, **i32)
+        self.src_slot = torch.empty(self.R, **i32)
+        if n_shared:
+            K, G = self.K, self.G
+            self.s_idx = torch.empty(T, K, **i32)
+            self.s_w = torch.empty(T, K, dtype=torch.float32, device=device)
+            self.s_counts = torch.empty(G, **i32)
+            self.s_off = torch.empty(G + 1, **i32)
+            self.s_dst = torch.empty(T * K, **i32)
+            self.s_src = torch.empty(R, **i32)
+        else:
+            self.s_idx, self.s_w, self.s_dst, self.s_src = self.topk_idx, self.topk_w, self.dst_row, self.src_slot
+            self.s_counts, self.s_off = self.counts, self.offsets
+        # group offsets and capacity the grouped GEMM takes (shared groups: explicit offsets)
+        self.g_cap = 0 if n_shared else capacity
         self.dev_err = torch.zeros(1, **i32)
         self.route_ws = torch.empty(moe_route_workspace_bytes(T, E, k), dtype=torch.uint8,
                                     device=device)
@@ -51,7 +73,7 @@ class MoELayer:
         self.y_perm = torch.empty(R, d, dtype=act, device=device)
         self.out = torch.empty(T, d, dtype=act, device=device)
         self.gemm_ws = None
-        wsb = moe_gemm_workspace_bytes(dtype, E, R, d, f)
+        wsb = moe_gemm_workspace_bytes(dtype, self.G, R, d, f)
         if wsb:
             self.gemm_ws = torch.empty(wsb, dtype=torch.uint8, device=device)
         self._bwd_alloc = False
@@ -59,7 +81,7 @@ class MoELayer:
     def _alloc_bwd(self):
         if self._bwd_alloc:
             return
-        R, d, f, E = self.n_rows, self.d, self.f, self.E
+        R, d, f, E = self.n_rows, self.d, self.f, self.G
         act = _ACT[self.dtype]
         dev = self.device
         self.dy_perm = torch.empty(R, d, dtype=act, device=dev)
@@ -78,7 +100,7 @@ class MoELayer:
         self._stages = None
         if self.dtype != MOE_MXFP8:
             return
-        E, f, d = self.E, self.f, self.d
+        E, f, d = self.G, self.f, self.d
         dev = self.device
         u8 = dict(dtype=torch.uint8, device=dev)
         # forward direction: blocks along the contraction dim of each GEMM
@@ -101,7 +123,7 @@ class MoELayer:
     def requantize_weights(self):
         """MXFP8: rebuild the four weight caches (forward and backward direction
         of w13 and w2) from the bf16 weights in place, as an optimizer step does."""
-        E, f, d = self.E, self.f, self.d
+        E, f, d = self.G, self.f, self.d
         moe_quantize_mxfp8(self.w13.reshape(E * 2 * f, d), 0, self.w13_q, self.w13_s)
         moe_quantize_mxfp8(self.w2.reshape(E * d, f), 0, self.w2_q, self.w2_s)
         moe_quantize_mxfp8(self.w13.reshape(E * 2 * f, d), 1, self.w13t_q, self.w13t_s, self._g13, E)
@@ -131,8 +153,8 @@ class MoELayer:
         if getattr(self, "_stages", None) is None:
             self._stages = self._stage_tensors()
         bwd = op in (MOE_GEMM_DGRAD_DOWN, MOE_GEMM_DGRAD_GATE_UP)
-        moe_grouped_gemm_op(op, self.dtype, self._stages[1 if bwd else 0], self.offsets,
-                            self.capacity, self.E, self.n_rows, self.d, self.f)
+        moe_grouped_gemm_op(op, self.dtype, self._stages[1 if bwd else 0], self.s_off,
+                            self.g_cap, self.G, self.n_rows, self.d, self.f)
 
     def wgrad_accumulate(self, dw13_f32, dw2_f32):
         """bf16: the weight-gradient stage adding into fp32 accumulators
@@ -141,32 +163,42 @@ class MoELayer:
         self._alloc_bwd()
         t = gemm_tensors(x_perm=self.x_perm, h=self.h, dy_perm=self.dy_perm, dgu=self.dgu,
                          dw13_f32=dw13_f32, dw2_f32=dw2_f32)
-        moe_grouped_gemm_op(MOE_GEMM_WGRAD, self.dtype, t, self.offsets, self.capacity, self.E,
+        moe_grouped_gemm_op(MOE_GEMM_WGRAD, self.dtype, t, self.s_off, self.g_cap, self.G,
                             self.n_rows, self.d, self.f)
 
     # -------------------------------------------------------------- steps
     def route(self, logits):
         moe_route_topk(logits, self.k, self.capacity, self.topk_idx, self.topk_w, self.counts,
                        self.offsets, self.dst_row, self.src_slot, self.route_ws, self.dev_err)
+        if self.S:
+            moe_route_add_shared(self.S, self.capacity, self.topk_idx, self.topk_w, self.dst_row,
+                                 self.counts, self.offsets, self.src_slot, self.s_idx, self.s_w,
+                                 self.s_counts, self.s_off, self.s_dst, self.s_src)
 
     def permute(self, x):
-        moe_permute(self.dtype, x, self.k, self.dst_row, self.x_perm, src_slot=self.src_slot,
+        moe_permute(self.dtype, x, self.K, self.s_dst, self.x_perm, src_slot=self.s_src,
                     x_perm_scales=self.x_perm_scales, dev_err=self.dev_err)
 
     def gemm_fwd(self):
         if self.dtype == MOE_MXFP8:
-            moe_grouped_gemm_fwd(self.dtype, self.x_perm, self.w13_q, self.w2_q, self.offsets,
-                                 self.capacity, self.gu, self.h, self.y_perm,
+            moe_grouped_gemm_fwd(self.dtype, self.x_perm, self.w13_q, self.w2_q, self.s_off,
+                                 self.g_cap, self.gu, self.h, self.y_perm,
                                  x_perm_scales=self.x_perm_scales, w13_scales=self.w13_s,
                                  w2_scales=self.w2_s, ws=self.gemm_ws)
         else:
-            moe_grouped_gemm_fwd(self.dtype, self.x_perm, self.w13, self.w2, self.offsets,
-                                 self.capacity, self.gu, self.h, self.y_perm)
+            moe_grouped_gemm_fwd(self.dtype, self.x_perm, self.w13, self.w2, self.s_off,
+                                 self.g_cap, self.gu, self.h, self.y_perm)
+
+    def _slot_weights(self, weights):
+        if weights is None or weights is self.s_w:
+            return self.s_w
+        assert not self.S, "per-row weights are not combined with shared experts"
+        return weights
 
     def combine(self, weights=None):
-        w = self.topk_w if weights is None else weights
         moe_unpermute_combine(MOE_F32 if self.dtype == MOE_F32 else MOE_BF16, self.y_perm,
-                              self.dst_row, w, self.k, self.out, dev_err=self.dev_err)
+                              self.s_dst, self._slot_weights(weights), self.K, self.out,
+                              dev_err=self.dev_err)
 
     def router_scores(self, x, w_router):
         """Router scores [T, E] fp32 = x . w_router^T (bf16 x and w_router [E, d])."""
@@ -194,19 +226,18 @@ class MoELayer:
     def backward(self, dout, weights=None):
         self._alloc_bwd()
         act_dt = MOE_F32 if self.dtype == MOE_F32 else MOE_BF16
-        w = self.topk_w if weights is None else weights
-        moe_permute(act_dt, dout, self.k, self.dst_row, self.dy_perm, src_slot=self.src_slot,
-                    row_scale=w, dev_err=self.dev_err)
+        moe_permute(act_dt, dout, self.K, self.s_dst, self.dy_perm, src_slot=self.s_src,
+                    row_scale=self._slot_weights(weights), dev_err=self.dev_err)
         if self.dtype == MOE_MXFP8:
             moe_grouped_gemm_bwd(self.dtype, self.dy_perm, self.x_perm, self.gu, self.h,
-                                 self.w13t_q, self.w2t_q, self.offsets, self.capacity, self.dgu,
+                                 self.w13t_q, self.w2t_q, self.s_off, self.g_cap, self.dgu,
                                  self.dx_perm, self.dw13, self.dw2,
                                  x_perm_scales=self.x_perm_scales, w13_scales=self.w13t_s,
                                  w2_scales=self.w2t_s, ws=self.gemm_ws)
         else:
             moe_grouped_gemm_bwd(self.dtype, self.dy_perm, self.x_perm, self.gu, self.h,
-                                 self.w13, self.w2, self.offsets, self.capacity, self.dgu,
+                                 self.w13, self.w2, self.s_off, self.g_cap, self.dgu,
                                  self.dx_perm, self.dw13, self.dw2)
-        moe_unpermute_combine(act_dt, self.dx_perm, self.dst_row, None, self.k, self.dx,
+        moe_unpermute_combine(act_dt, self.dx_perm, self.s_dst, None, self.K, self.dx,
                               dev_err=self.dev_err)
         return self.dx, self.dw13, self.dw2

@@ -38,6 +38,41 @@ def oracle_layer(inp, k, capacity=0, round_mode=oracle.BF16, bwd=True, weights=N
     return res
 
 
+def oracle_layer_shared(inp, k, n_shared, capacity=0, round_mode=oracle.BF16, bwd=True):
+    """The layer with n_shared shared experts, read as ungated extra experts
+    E .. E+n_shared-1 that every token uses with weight 1 (inp["w13"], inp["w2"]
+    hold E + n_shared experts, the shared ones last): the oracle's own route,
+    then its permute / FFN / combine over the k + n_shared slots of each token,
+    the shared rows after the routed ones (row R + s*T + t)."""
+    logits = inp["logits"].detach().cpu().numpy()
+    T, E = logits.shape
+    S, K = n_shared, k + n_shared
+    r = oracle.route(logits, k, capacity)
+    R = r["n_rows"]
+    n = R + S * T
+    dst = np.empty((T, K), np.int32)
+    dst[:, :k] = r["dst_row"].reshape(T, k)
+    w = np.ones((T, K), np.float32)
+    w[:, :k] = r["topk_w"]
+    for s_ in range(S):
+        dst[:, k + s_] = R + s_ * T + np.arange(T)
+    dst = dst.reshape(-1)
+    go = np.concatenate([oracle.group_offsets(r["offsets"], capacity),
+                         R + T * np.arange(1, S + 1)]).astype(np.int32)
+    x, w13, w2 = np64(inp["x"]), np64(inp["w13"]), np64(inp["w2"])
+    xp = oracle.permute(x, dst, K, n)
+    gu, h, y = oracle.ffn_fwd(xp, w13, w2, go, round_mode)
+    out = oracle.combine(y, dst, w, T, K, round_mode)
+    res = dict(route=r, dst=dst, w=w, go=go, x_perm=xp, gu=gu, h=h, y_perm=y, out=out)
+    if bwd:
+        dout = np64(inp["dout"])
+        dy = oracle.permute(dout, dst, K, n, row_scale=w, round_mode=round_mode)
+        dgu, dxp, dw13, dw2 = oracle.ffn_bwd(dy, xp, gu, h, w13, w2, go, round_mode)
+        dx = oracle.combine(dxp, dst, None, T, K, round_mode)
+        res.update(dy_perm=dy, dgu=dgu, dx_perm=dxp, dw13=dw13, dw2=dw2, dx=dx)
+    return res
+
+
 def rel_err(gpu, ref):
     """max|gpu - ref| / max|ref| (0 for empty tensors)."""
     g = np.asarray(gpu, np.float64)

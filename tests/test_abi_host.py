@@ -184,6 +184,21 @@ def test_router_and_gate_grad_validation(m):
     assert gg(T=0, n_rows=0, dout=None, y=None, dl=None) == m.MOE_OK
 
 
+def test_route_add_shared_validation(m):
+    lib = m.load()
+    P = FAKE
+
+    def call(T=100, E=8, k=2, S=1, C=0, n_rows=200, counts=P, src=P):
+        return lib.moe_route_add_shared(T, E, k, S, C, P, P, P, counts, P, src, n_rows, P, P, P, P, P, P, None)
+    assert call(S=0) == m.MOE_EINVAL
+    assert call(k=7, S=2) == m.MOE_EINVAL          # k + n_shared > 8
+    assert call(E=1024, S=1) == m.MOE_EINVAL       # E + n_shared > 1024
+    assert call(n_rows=199) == m.MOE_EINVAL        # not the route's row count
+    assert call(C=30, n_rows=200) == m.MOE_EINVAL  # padded: n_rows = E*C
+    assert call(counts=None) == m.MOE_EINVAL
+    assert call(src=None) == m.MOE_EINVAL
+
+
 def test_wgrad_fp32_accumulate_validation(m):
     lib = m.load()
     P = FAKE

@@ -13,7 +13,7 @@ import torch
 
 import moe_synth
 import oracle
-from tests._chain import BF16_TOL, F32_TOL, assert_close, np64, oracle_layer
+from tests._chain import BF16_TOL, F32_TOL, assert_close, np64, oracle_layer, oracle_layer_shared
 
 pytestmark = pytest.mark.gpu
 
@@ -197,6 +197,46 @@ def test_wgrad_fp32_accumulate(moe, T, d, E, f, k, C):
         assert torch.equal(a13[E - 2], s13[E - 2]) and torch.equal(a2[E - 2], s2[E - 2])
     # the bf16 gradients of the same backward are untouched
     assert_close(np64(lay.dw13), ref["dw13"], BF16_TOL, "dw13")
+
+
+SHARED_CASES = [
+    # T, d, E, f, k, shared experts, capacity
+    (384, 256, 5, 384, 2, 1, 0),
+    (256, 128, 8, 128, 2, 2, 0),
+    (400, 128, 8, 128, 2, 1, 70),
+    (300, 64, 4, 64, 1, 1, 0),
+]
+
+
+@pytest.mark.parametrize("T,d,E,f,k,S,C", SHARED_CASES)
+def test_layer_shared_experts_parity(moe, T, d, E, f, k, S, C):
+    # shared experts as extra groups E .. E+S-1 of the same grouped GEMM
+    from routing_grouped_gemm_amd.layer import MoELayer
+    _say("shared", T, d, E, f, k, S, C)
+    inp = moe_synth.make_inputs(T=T, d=d, E=E + S, f=f, k=k, seed=T + 5 * S + C)
+    inp["logits"] = inp["logits"][:, :E].contiguous()
+    lay = MoELayer(T, d, E, f, k, moe.MOE_BF16, capacity=C, n_shared=S)
+    g = {n: inp[n].to(DEV) for n in ("logits", "x", "w13", "w2", "dout")}
+    lay.set_weights(g["w13"], g["w2"])
+    lay.forward(g["logits"], g["x"])
+    lay.backward(g["dout"])
+    torch.cuda.synchronize()
+    assert int(lay.dev_err.item()) == 0
+    ref = oracle_layer_shared(inp, k, S, capacity=C, round_mode=oracle.BF16)
+    # the widened route is integer data: bit-exact
+    np.testing.assert_array_equal(lay.s_dst.cpu().numpy(), ref["dst"])
+    sw = lay.s_w.cpu().numpy()
+    assert np.all(sw[:, k:] == 1.0)                        # shared slots: weight exactly 1
+    np.testing.assert_allclose(sw[:, :k], ref["w"][:, :k], rtol=0, atol=1e-6)   # as the route tests
+    np.testing.assert_array_equal(lay.s_off.cpu().numpy(), ref["go"])
+    np.testing.assert_array_equal(np64(lay.x_perm), ref["x_perm"])
+    assert_close(np64(lay.out), ref["out"], BF16_TOL, "out")
+    assert_close(np64(lay.dx), ref["dx"], BF16_TOL, "dx")
+    assert_close(np64(lay.dw13), ref["dw13"], BF16_TOL, "dw13")
+    assert_close(np64(lay.dw2), ref["dw2"], BF16_TOL, "dw2")
+    # the shared experts' own weight gradients, on their own scale
+    assert_close(np64(lay.dw13[E:]), ref["dw13"][E:], BF16_TOL, "dw13 shared")
+    assert_close(np64(lay.dw2[E:]), ref["dw2"][E:], BF16_TOL, "dw2 shared")
 
 
 def test_layer_deterministic(moe):

@@ -202,3 +202,25 @@ def test_bf16_storage_rounding_points(oracle_lib):
         np.testing.assert_array_equal(o.round_(b, o.BF16), b)   # representable in bf16
         scale = np.abs(a).max()
         assert np.abs(a - b).max() <= 2 ** -7 * scale * 4
+
+
+@pytest.mark.parametrize("S,C", [(1, 0), (2, 0), (1, 40)])
+def test_shared_experts_add_a_dense_ffn(oracle_lib, S, C):
+    # a shared expert is an ungated expert every token uses: the layer with
+    # shared experts equals the routed layer plus, per shared expert, the
+    # dense SwiGLU FFN of x with that expert's weights (fp64, no rounding)
+    import moe_synth
+    from tests._chain import np64, oracle_layer, oracle_layer_shared
+    T, d, E, f, k = 48, 16, 4, 24, 2
+    inp = moe_synth.make_inputs(T=T, d=d, E=E + S, f=f, k=k, dtype="f32", seed=11 + S)
+    inp["logits"] = inp["logits"][:, :E].contiguous()
+    full = oracle_layer_shared(inp, k, S, capacity=C, round_mode=oracle_lib.NONE, bwd=False)
+    routed_inp = dict(inp, w13=inp["w13"][:E], w2=inp["w2"][:E])
+    routed = oracle_layer(routed_inp, k, capacity=C, round_mode=oracle_lib.NONE, bwd=False)
+    x = np64(inp["x"])
+    dense = np.zeros_like(x)
+    for s_ in range(S):
+        w13 = np64(inp["w13"][E + s_:E + s_ + 1])
+        w2 = np64(inp["w2"][E + s_:E + s_ + 1])
+        dense += oracle_lib.ffn_fwd(x, w13, w2, np.array([0, T], np.int32), oracle_lib.NONE)[2]
+    np.testing.assert_allclose(full["out"], routed["out"] + dense, rtol=1e-12, atol=1e-14)
