@@ -38,6 +38,16 @@
 // the same loop for the weight-gradient GEMM (both operands MN-major, every
 // fragment two transposed LDS reads); measured about 5% slower there than the
 // single-group loop at 256 x 256 tiles over experts of ~512 rows
+// weight-gradient tiles dealt to the XCDs in runs of this many tiles (0: a
+// contiguous range per XCD).  A weight-gradient tile's cost is its group's
+// row count, so with uneven groups (Zipf routing, shared experts) contiguous
+// ranges leave one XCD with the big groups: e128 under Zipf(1.2) 9.97 ->
+// 2.97 ms, one shared expert 5.86 -> 3.70 ms; uniform e128 2.93 -> 2.97 ms
+// (each XCD's L2 then sees every expert).  Runs of 16 measured the same, 32
+// slower.
+#ifndef MOE_GEMM_K_DEAL
+#define MOE_GEMM_K_DEAL 4
+#endif
 // single-group loop with both operands MN-major (the weight gradient): the
 // next k-slice's fragment reads go between the MFMAs instead of in a burst
 #ifndef MOE_GEMM_READ_INTERLEAVE
@@ -675,11 +685,20 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_kernel(KParams p)
     const int t0 = p.pr[0].mtn * p.pr[0].ntn;
     const int tiles_e = t0 + (p.nprob > 1 ? p.pr[1].mtn * p.pr[1].ntn : 0);
     const int total = p.E * tiles_e;
-    const int per_xcd = (total + 7) / 8;
     const int xcd = blockIdx.x % 8;
     const int slot = blockIdx.x / 8;
+#if MOE_GEMM_K_DEAL
+    // runs of MOE_GEMM_K_DEAL tiles dealt round-robin to the XCDs: every
+    // group's tiles, whatever its row count (the K of its tiles), spread
+    // over all XCDs
+    constexpr int RUN = MOE_GEMM_K_DEAL;
+    const int run = slot / RUN;
+    const int L = (run * 8 + xcd) * RUN + slot % RUN;
+#else
+    const int per_xcd = (total + 7) / 8;
     if (slot >= per_xcd) return;
     const int L = xcd * per_xcd + slot;
+#endif
     if (L >= total) return;
     const int e = L / tiles_e;
     int local = L - e * tiles_e;
@@ -850,7 +869,12 @@ hipError_t launch_k(const KParams& p, hipStream_t s)
     int64_t tiles_e = 0;
     for (int i = 0; i < p.nprob; ++i) tiles_e += (int64_t)p.pr[i].mtn * p.pr[i].ntn;
     const int64_t total = (int64_t)p.E * tiles_e;
+#if MOE_GEMM_K_DEAL
+    // whole runs on each of the 8 XCDs
+    const int64_t grid = (total + 8 * MOE_GEMM_K_DEAL - 1) / (8 * MOE_GEMM_K_DEAL) * (8 * MOE_GEMM_K_DEAL);
+#else
     const int64_t grid = (total + 7) / 8 * 8;
+#endif
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL((gemm_grouped_k_kernel<BM, BK, NS, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
     return hipGetLastError();
