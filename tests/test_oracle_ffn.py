@@ -224,3 +224,31 @@ def test_shared_experts_add_a_dense_ffn(oracle_lib, S, C):
         w2 = np64(inp["w2"][E + s_:E + s_ + 1])
         dense += oracle_lib.ffn_fwd(x, w13, w2, np.array([0, T], np.int32), oracle_lib.NONE)[2]
     np.testing.assert_allclose(full["out"], routed["out"] + dense, rtol=1e-12, atol=1e-14)
+
+
+def test_shared_experts_equal_one_wider_expert(oracle_lib):
+    # several ungated shared experts act as one expert of their summed width:
+    # SwiGLU is elementwise over the hidden units and the down projection sums
+    # over them, so S experts of width f equal one of width S*f whose gate
+    # rows, up rows and down columns are the S experts' stacked (fp64, exact
+    # up to summation order)
+    import moe_synth
+    from tests._chain import np64, oracle_layer_shared
+    T, d, E, f, k, S = 40, 16, 4, 12, 2, 3
+    inp = moe_synth.make_inputs(T=T, d=d, E=E + S, f=f, k=k, dtype="f32", seed=29)
+    inp["logits"] = inp["logits"][:, :E].contiguous()
+    full = oracle_layer_shared(inp, k, S, round_mode=oracle_lib.NONE, bwd=False)
+    w13, w2 = np64(inp["w13"]), np64(inp["w2"])
+    gate = np.concatenate([w13[E + s, :f] for s in range(S)])      # [S*f, d]
+    up = np.concatenate([w13[E + s, f:] for s in range(S)])
+    wide13 = np.concatenate([gate, up])[None]                      # [1, 2*S*f, d]
+    wide2 = np.concatenate([w2[E + s] for s in range(S)], axis=1)[None]   # [1, d, S*f]
+    x = np64(inp["x"])
+    wide = oracle_lib.ffn_fwd(x, wide13, wide2, np.array([0, T], np.int32), oracle_lib.NONE)[2]
+    # the routed part: the layer with the shared experts' outputs taken away
+    y = full["y_perm"]
+    R = full["route"]["n_rows"]
+    routed_part = full["out"] - sum(y[R + s * T:R + (s + 1) * T] for s in range(S))
+    scale = np.abs(wide).max()
+    assert scale > 0, "the wide expert's output is not the trivial zero"
+    np.testing.assert_allclose(routed_part + wide, full["out"], rtol=1e-12, atol=1e-12 * scale)
