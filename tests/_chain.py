@@ -38,18 +38,14 @@ def oracle_layer(inp, k, capacity=0, round_mode=oracle.BF16, bwd=True, weights=N
     return res
 
 
-def oracle_layer_shared(inp, k, n_shared, capacity=0, round_mode=oracle.BF16, bwd=True):
-    """The layer with n_shared shared experts, read as ungated extra experts
-    E .. E+n_shared-1 that every token uses with weight 1 (inp["w13"], inp["w2"]
-    hold E + n_shared experts, the shared ones last): the oracle's own route,
-    then its permute / FFN / combine over the k + n_shared slots of each token,
-    the shared rows after the routed ones (row R + s*T + t)."""
-    logits = inp["logits"].detach().cpu().numpy()
-    T, E = logits.shape
+def widen_route(r, k, n_shared, capacity=0):
+    """The oracle route r widened by n_shared shared experts: slot k+s of token
+    t goes to row R + s*T + t with weight 1, the shared groups after the routed
+    ones.  Returns dst [T*(k+S)], w [T, k+S], group offsets [E+S+1] and
+    src [R+S*T] (the slot of each row, -1 for padding)."""
     S, K = n_shared, k + n_shared
-    r = oracle.route(logits, k, capacity)
+    T = r["topk_idx"].shape[0]
     R = r["n_rows"]
-    n = R + S * T
     dst = np.empty((T, K), np.int32)
     dst[:, :k] = r["dst_row"].reshape(T, k)
     w = np.ones((T, K), np.float32)
@@ -59,6 +55,24 @@ def oracle_layer_shared(inp, k, n_shared, capacity=0, round_mode=oracle.BF16, bw
     dst = dst.reshape(-1)
     go = np.concatenate([oracle.group_offsets(r["offsets"], capacity),
                          R + T * np.arange(1, S + 1)]).astype(np.int32)
+    src = -np.ones(R + S * T, np.int32)
+    live = dst >= 0
+    src[dst[live]] = np.nonzero(live)[0]
+    return dst, w, go, src
+
+
+def oracle_layer_shared(inp, k, n_shared, capacity=0, round_mode=oracle.BF16, bwd=True):
+    """The layer with n_shared shared experts, read as ungated extra experts
+    E .. E+n_shared-1 that every token uses with weight 1 (inp["w13"], inp["w2"]
+    hold E + n_shared experts, the shared ones last): the oracle's own route,
+    then its permute / FFN / combine over the k + n_shared slots of each token,
+    the shared rows after the routed ones (row R + s*T + t)."""
+    logits = inp["logits"].detach().cpu().numpy()
+    T = logits.shape[0]
+    S, K = n_shared, k + n_shared
+    r = oracle.route(logits, k, capacity)
+    dst, w, go, _ = widen_route(r, k, S, capacity)
+    n = int(go[-1])
     x, w13, w2 = np64(inp["x"]), np64(inp["w13"]), np64(inp["w2"])
     xp = oracle.permute(x, dst, K, n)
     gu, h, y = oracle.ffn_fwd(xp, w13, w2, go, round_mode)

@@ -25,7 +25,7 @@ import torch
 
 import moe_synth
 import oracle
-from tests._chain import BF16_TOL, assert_close, np64
+from tests._chain import BF16_TOL, assert_close, np64, widen_route
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,7 @@ def _say(*a):
     sys.stdout.flush()
 
 
-CASES = [("e8", False), ("e128", False), ("e128_zipf", False), ("e128_zipf", True)]
+CASES = [("e8", False), ("e128", False), ("e128_zipf", False), ("e128_zipf", True), ("e128_shared", False)]
 
 
 @pytest.fixture(scope="module")
@@ -53,7 +53,7 @@ def _run(m, name, padded):
     T, d, E, f, k = cfg["T"], cfg["d"], cfg["E"], cfg["f"], cfg["k"]
     cap = moe_synth.capacity_of(T, k, E, cfg.get("capacity_factor", 1.25)) if padded else 0
     inp = moe_synth.make_inputs(name, device="cuda")
-    lay = MoELayer(T, d, E, f, k, m.MOE_BF16, capacity=cap)
+    lay = MoELayer(T, d, E, f, k, m.MOE_BF16, capacity=cap, n_shared=cfg.get("n_shared", 0))
     lay.set_weights(inp["w13"], inp["w2"])
     lay.forward(inp["logits"], inp["x"])
     lay.backward(inp["dout"])
@@ -87,9 +87,18 @@ def test_fullsize_layer(moe, name, padded):
     np.testing.assert_array_equal(lay.dst_row.cpu().numpy(), r["dst_row"])
     np.testing.assert_array_equal(lay.src_slot.cpu().numpy(), r["src_slot"])
     np.testing.assert_allclose(lay.topk_w.cpu().numpy(), r["topk_w"], rtol=0, atol=1e-6)
-    go = oracle.group_offsets(r["offsets"], cap)
-    src = r["src_slot"]
-    w_pair = r["topk_w"].reshape(-1)
+    # shared experts: slots k .. k+S-1 of every token, groups E .. E+S-1
+    S = cfg.get("n_shared", 0)
+    dst_all, w_all, go, src = widen_route(r, k, S, cap)
+    if not S:
+        np.testing.assert_array_equal(src, r["src_slot"])
+    else:
+        np.testing.assert_array_equal(lay.s_dst.cpu().numpy(), dst_all)
+        np.testing.assert_array_equal(lay.s_src.cpu().numpy(), src)
+        np.testing.assert_array_equal(lay.s_off.cpu().numpy(), go)
+        assert np.all(lay.s_w.cpu().numpy()[:, k:] == 1.0)
+    k = k + S                                   # slots per token from here on
+    w_pair = w_all.reshape(-1)
     rng = np.random.default_rng(sum(map(ord, name)) * 2 + int(padded))
     rows = [i for i in _sample_rows(go, rng) if src[i] >= 0]
     row_expert = np.searchsorted(go, rows, side="right") - 1
@@ -163,7 +172,7 @@ def test_fullsize_layer(moe, name, padded):
     for t in t_sel:
         ys, dxs = np.zeros(d), np.zeros(d)
         for j in range(k):
-            dst = r["dst_row"][t * k + j]
+            dst = dst_all[t * k + j]
             if dst < 0:
                 continue
             e = int(np.searchsorted(go, dst, side="right") - 1)

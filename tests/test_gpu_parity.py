@@ -229,6 +229,18 @@ def test_layer_shared_experts_parity(moe, T, d, E, f, k, S, C):
     assert np.all(sw[:, k:] == 1.0)                        # shared slots: weight exactly 1
     np.testing.assert_allclose(sw[:, :k], ref["w"][:, :k], rtol=0, atol=1e-6)   # as the route tests
     np.testing.assert_array_equal(lay.s_off.cpu().numpy(), ref["go"])
+    idx = lay.s_idx.cpu().numpy()
+    np.testing.assert_array_equal(idx[:, :k], ref["route"]["topk_idx"])
+    np.testing.assert_array_equal(idx[:, k:], np.broadcast_to(E + np.arange(S), (T, S)))
+    cnt = lay.s_counts.cpu().numpy()
+    np.testing.assert_array_equal(cnt[:E], ref["route"]["counts"])
+    assert np.all(cnt[E:] == T)
+    # src_slot is the inverse of dst_row over the widened slots; pad rows hold -1
+    src = lay.s_src.cpu().numpy()
+    expect = -np.ones(src.size, np.int64)
+    live = ref["dst"] >= 0
+    expect[ref["dst"][live]] = np.nonzero(live)[0]
+    np.testing.assert_array_equal(src, expect)
     np.testing.assert_array_equal(np64(lay.x_perm), ref["x_perm"])
     assert_close(np64(lay.out), ref["out"], BF16_TOL, "out")
     assert_close(np64(lay.dx), ref["dx"], BF16_TOL, "dx")
