@@ -38,13 +38,14 @@
 // the same loop for the weight-gradient GEMM (both operands MN-major, every
 // fragment two transposed LDS reads); measured about 5% slower there than the
 // single-group loop at 256 x 256 tiles over experts of ~512 rows
-// weight-gradient tiles dealt to the XCDs in runs of this many tiles (0: a
-// contiguous range per XCD).  A weight-gradient tile's cost is its group's
-// row count, so with uneven groups (Zipf routing, shared experts) contiguous
-// ranges leave one XCD with the big groups: e128 under Zipf(1.2) 9.97 ->
-// 2.97 ms, one shared expert 5.86 -> 3.70 ms; uniform e128 2.93 -> 2.97 ms
-// (each XCD's L2 then sees every expert).  Runs of 16 measured the same, 32
-// slower.
+// weight-gradient tiles dealt to the XCDs in runs of this many tiles when
+// contiguous ranges would load them unevenly (0: always contiguous).  A
+// weight-gradient tile's cost is its group's row count, so with uneven
+// groups (Zipf routing, shared experts) contiguous ranges leave one XCD with
+// the big groups: e128 under Zipf(1.2) 9.97 -> 2.97 ms, one shared expert
+// 5.86 -> 3.70 ms.  Dealt always, uniform e128 went 2.93 -> 2.97 ms with 2.9x
+// the HBM reads (each XCD's L2 then sees every expert), hence the test.
+// Runs of 16 measured the same, 32 slower.
 #ifndef MOE_GEMM_K_DEAL
 #define MOE_GEMM_K_DEAL 4
 #endif
@@ -675,6 +676,53 @@ struct KParams {
     int64_t n_rows;
 };
 
+// Whether contiguous tile ranges would load the XCDs unevenly: a weight-gradient
+// tile costs about its group's row count (its K) plus a fixed overhead
+// (setup, first loads, output store) worth some 256 rows; uneven means the
+// busiest XCD's share exceeds the mean by more than 5%.  One wave computes it
+// from the group offsets (k_deal_flag_kernel below).
+__device__ __forceinline__ bool k_tiles_uneven(const KParams& p, int tiles_e, int per_xcd)
+{
+    constexpr float kTileCostRows = 256.f;
+    const int lane = threadIdx.x & 63;
+    float xc[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) xc[x] = 0.f;
+    for (int e = lane; e < p.E; e += 64) {
+        const float c = (float)group_rows(p.group_off, p.capacity, e, p.n_rows) + kTileCostRows;
+        const int64_t a = (int64_t)e * tiles_e, b = a + tiles_e;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            const int64_t lo = max(a, (int64_t)x * per_xcd), hi = min(b, (int64_t)(x + 1) * per_xcd);
+            if (hi > lo) xc[x] += (float)(hi - lo) * c;
+        }
+    }
+    float mx = 0.f, sum = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+        float v = xc[x];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+        mx = fmaxf(mx, v);
+        sum += v;
+    }
+    // lanes may round the sums differently: lane 0 decides for the wave
+    return __builtin_amdgcn_readfirstlane(mx > 1.05f * (sum * 0.125f) ? 1 : 0) != 0;
+}
+
+// 1 if the weight-gradient tiles are dealt to the XCDs in runs, 0 for
+// contiguous ranges: written by k_deal_flag_kernel ahead of every
+// weight-gradient launch on the same stream.  Both mappings cover every tile
+// once, so launches that overlap on one device can at worst make each other
+// take the slower mapping, never a wrong result.
+__device__ int g_k_deal;
+
+__global__ __launch_bounds__(64) void k_deal_flag_kernel(KParams p, int tiles_e, int per_xcd)
+{
+    const bool d = k_tiles_uneven(p, tiles_e, per_xcd);
+    if (threadIdx.x == 0) g_k_deal = d ? 1 : 0;
+}
+
 // Grouped-K GEMM (weight gradients): C_e = A_e^T B_e over the rows of group e,
 // for one or two problems sharing the groups.  Tiles are expert-major so the
 // tiles reading one expert's rows run together on one XCD.
@@ -687,28 +735,41 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_kernel(KParams p)
     const int total = p.E * tiles_e;
     const int xcd = blockIdx.x % 8;
     const int slot = blockIdx.x / 8;
-#if MOE_GEMM_K_DEAL
-    // runs of MOE_GEMM_K_DEAL tiles dealt round-robin to the XCDs: every
-    // group's tiles, whatever its row count (the K of its tiles), spread
-    // over all XCDs
-    constexpr int RUN = MOE_GEMM_K_DEAL;
-    const int run = slot / RUN;
-    const int L = (run * 8 + xcd) * RUN + slot % RUN;
-#else
     const int per_xcd = (total + 7) / 8;
-    if (slot >= per_xcd) return;
-    const int L = xcd * per_xcd + slot;
-#endif
+    // a contiguous range per XCD: its L2 serves a few groups' operands
+    const int Lc = slot < per_xcd ? xcd * per_xcd + slot : total;
+#if MOE_GEMM_K_DEAL
+    // or runs of MOE_GEMM_K_DEAL tiles dealt round-robin to the XCDs, so that
+    // every group's tiles, whatever its row count (the K of its tiles), spread
+    // over all XCDs, as the flag kernel decided.  The group bounds of both
+    // candidate tiles are read with the flag (selected, not branched on, so
+    // the loads stay together): one memory round trip, as for a fixed mapping.
+    constexpr int RUN = MOE_GEMM_K_DEAL;
+    const int Ld = ((slot / RUN) * 8 + xcd) * RUN + slot % RUN;
+    const int ec = min(Lc, total - 1) / tiles_e, ed = min(Ld, total - 1) / tiles_e;
+    const int64_t gc0 = group_begin(p.group_off, p.capacity, ec, p.n_rows);
+    const int64_t gc1 = group_begin(p.group_off, p.capacity, ec + 1, p.n_rows);
+    const int64_t gd0 = group_begin(p.group_off, p.capacity, ed, p.n_rows);
+    const int64_t gd1 = group_begin(p.group_off, p.capacity, ed + 1, p.n_rows);
+    const bool deal = g_k_deal != 0;
+    const int L = deal ? Ld : Lc;
     if (L >= total) return;
     const int e = L / tiles_e;
+    const int64_t g0 = deal ? gd0 : gc0;
+    const int m_e = (int)max((int64_t)0, deal ? gd1 - gd0 : gc1 - gc0);
+#else
+    const int L = Lc;
+    if (L >= total) return;
+    const int e = L / tiles_e;
+    const int64_t g0 = group_begin(p.group_off, p.capacity, e, p.n_rows);
+    const int m_e = (int)group_rows(p.group_off, p.capacity, e, p.n_rows);
+#endif
     int local = L - e * tiles_e;
     const int which = local < t0 ? 0 : 1;
     if (which) local -= t0;
     const KProblem& q = p.pr[which];
     int mt, nt;
     grouped_tile(local, q.mtn, q.ntn, 4, mt, nt);
-    const int64_t g0 = group_begin(p.group_off, p.capacity, e, p.n_rows);
-    const int m_e = (int)group_rows(p.group_off, p.capacity, e, p.n_rows);
 
     TileSrc sa;
     sa.p0 = sa.p1 = q.A + g0 * q.lda + (int64_t)mt * BM;
@@ -876,6 +937,9 @@ hipError_t launch_k(const KParams& p, hipStream_t s)
     const int64_t grid = (total + 7) / 8 * 8;
 #endif
     if (grid == 0) return hipSuccess;
+#if MOE_GEMM_K_DEAL
+    hipLaunchKernelGGL(k_deal_flag_kernel, dim3(1), dim3(64), 0, s, p, (int)tiles_e, (int)((total + 7) / 8));
+#endif
     hipLaunchKernelGGL((gemm_grouped_k_kernel<BM, BK, NS, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
     return hipGetLastError();
 }
