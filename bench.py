@@ -233,11 +233,38 @@ def run_gpu(args, cfg):
     gpu_ms = sum(evs[i][0].elapsed_time(evs[i][len(STAGES)]) for i in range(K)) / K
     ms_per_step = wall * 1e3 / K
     counts = lay.counts.cpu()
+    graph = graph_replay(step, K, T)
     f1 = router_steps(lay, inp, K) if dt == m.MOE_BF16 and not cap else None
     f4 = wgrad_f32_accumulate(lay, K) if dt == m.MOE_BF16 and not cap else None
     wq = weight_requant(lay, K) if dt == m.MOE_MXFP8 else None
     return dict(stage_ms=stage_ms, gpu_ms=gpu_ms, ms_per_step=ms_per_step, R=R, cap=cap, f1=f1, wq=wq, f4=f4,
+                graph=graph,
                 counts=counts, inp=inp, lay=lay)
+
+
+def graph_replay(step, reps, T):
+    """The same step captured once in a HIP graph and replayed `reps` times
+    (wall clock around the replays, synchronised on both sides): the launch
+    path without per-kernel host overhead.  Reported beside the eager step."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(None)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(None)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    del g
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms / 1e3), 1)}
 
 
 def router_steps(lay, inp, reps):
@@ -466,6 +493,7 @@ def main():
         "roofline": rl,
         "expert_rows": {"min": int(res["counts"].min()), "max": int(res["counts"].max())},
     }
+    out["graph_replay"] = res["graph"]
     if res["f1"]:
         out["router_and_gate_grad"] = res["f1"]
     if res["wq"]:
