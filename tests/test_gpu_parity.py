@@ -274,3 +274,25 @@ def test_permute_row_range_error_is_flagged(moe):
     ok = torch.ones(T * k, dtype=torch.bool)
     ok[5] = False
     assert torch.equal(xp.cpu()[ok], x.cpu().repeat_interleave(k, 0)[ok])
+
+
+@pytest.mark.parametrize("S", [0, 1])
+def test_layer_empty_batch(moe, S):
+    # no tokens: every group (shared ones included) is empty, the outputs are
+    # empty and the weight gradients exactly zero
+    from routing_grouped_gemm_amd.layer import MoELayer
+    _say("layer-empty", S)
+    T, d, E, f, k = 0, 128, 8, 128, 2
+    inp = moe_synth.make_inputs(T=4, d=d, E=E + S, f=f, k=k, seed=21)
+    lay = MoELayer(T, d, E, f, k, moe.MOE_BF16, n_shared=S)
+    lay.set_weights(inp["w13"].to(DEV), inp["w2"].to(DEV))
+    x = torch.empty(0, d, dtype=torch.bfloat16, device=DEV)
+    out = lay.forward(torch.empty(0, E, device=DEV), x)
+    dx, dw13, dw2 = lay.backward(torch.empty(0, d, dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert int(lay.dev_err.item()) == 0
+    assert out.shape == (0, d) and dx.shape == (0, d)
+    assert dw13.shape == (E + S, 2 * f, d) and dw2.shape == (E + S, d, f)
+    assert torch.all(dw13 == 0) and torch.all(dw2 == 0)
+    assert torch.all(lay.s_off == 0)
+    assert torch.all(lay.s_counts == 0)

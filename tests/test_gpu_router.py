@@ -177,3 +177,21 @@ def test_gate_grad_full_size_sampled_tokens(moe):
     moe.moe_permute(moe.MOE_BF16, dout, k, r["dst_row"], ref, src_slot=r["src_slot"], row_scale=r["topk_w"])
     torch.cuda.synchronize()
     assert torch.equal(dyp, ref)
+
+
+def test_router_and_gate_grad_empty(moe):
+    # no tokens: both calls succeed and write nothing
+    _say("router-empty")
+    E, d, k = 8, 64, 2
+    w = torch.randn(E, d, device=DEV).to(torch.bfloat16)
+    x = torch.empty(0, d, dtype=torch.bfloat16, device=DEV)
+    lg = torch.empty(0, E, dtype=torch.float32, device=DEV)
+    moe.moe_router_logits(x, w, lg)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, **i32)
+    moe.moe_gate_grad(torch.empty(0, d, dtype=torch.bfloat16, device=DEV),
+                      torch.empty(0, d, dtype=torch.bfloat16, device=DEV), torch.empty(0, k, **i32),
+                      torch.empty(0, k, dtype=torch.float32, device=DEV), torch.empty(0, **i32),
+                      torch.empty(0, E, dtype=torch.float32, device=DEV), dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
