@@ -45,11 +45,11 @@ KERNEL_NAMES = {
     "route": "route_topk_kernel + route_scan_kernel + route_finalize_kernel",
 }
 KERNEL_NAMES_MX = {
-    "gemm_gate_up": "mx_grouped_m_kernel<256, 1> (gate/up + SwiGLU)",
-    "gemm_down": "quant_rows_kernel (h) + mx_grouped_m_kernel<256, 0> (down)",
-    "gemm_dgrad_down": "quant_rows_kernel (dy) + mx_grouped_m_kernel<256, 2> (dgrad down + SwiGLU bwd)",
-    "gemm_dgrad_gate_up": "quant_rows_kernel (dgu) + mx_grouped_m_kernel<256, 0> (dgrad gate/up)",
-    "gemm_wgrad": "4 x quant_cols_kernel + mx_grouped_k_kernel<256> (wgrad, dWd and dW13)",
+    "gemm_gate_up": "mx_grouped_m_kernel<256, 1, 8> (gate/up + SwiGLU)",
+    "gemm_down": "quant_rows_kernel (h) + mx_grouped_m_kernel<256, 0, 8> (down)",
+    "gemm_dgrad_down": "quant_rows_kernel (dy) + mx_grouped_m_kernel<256, 2, 8> (dgrad down + SwiGLU bwd)",
+    "gemm_dgrad_gate_up": "quant_rows_kernel (dgu) + mx_grouped_m_kernel<256, 0, 8> (dgrad gate/up)",
+    "gemm_wgrad": "4 x quant_cols_kernel + mx_grouped_k_kernel<256, 8> (wgrad, dWd and dW13)",
     "permute": "permute_mx_kernel",
     "combine": "combine_kernel<true, {k}>",
     "combine_bwd": "permute_kernel<true, true, {k}>",
