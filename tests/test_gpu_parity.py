@@ -124,6 +124,7 @@ LAYER_CASES = [
     (1100, 256, 4, 256, 1, "bf16", 0),
     (160, 128, 6, 128, 2, "bf16", 0),
     (1400, 256, 4, 256, 1, "bf16", 0),
+    (600, 128, 1024, 64, 8, "bf16", 0),     # the most experts and slots: ~5 rows per expert
 ]
 
 
@@ -205,6 +206,7 @@ SHARED_CASES = [
     (256, 128, 8, 128, 2, 2, 0),
     (400, 128, 8, 128, 2, 1, 70),
     (300, 64, 4, 64, 1, 1, 0),
+    (300, 128, 1023, 64, 7, 1, 0),      # E + S = 1024 groups, k + S = 8 slots
 ]
 
 
