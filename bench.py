@@ -434,7 +434,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} is not "
-              "supported (this build runs on exactly one GPU).", file=sys.stderr)
+              "supported (the path and its measurement run on exactly one GPU).", file=sys.stderr)
         sys.exit(2)
 
     import moe_synth
