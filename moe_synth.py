@@ -36,6 +36,9 @@ WORKLOADS = {
     # e128 plus one shared expert (ungated, every token) of the same width
     "e128_shared": dict(idx=6, T=16384, d=4096, E=128, f=1536, k=4, n_shared=1, dtype="bf16",
                         routing="uniform", bwd=True),
+    # the MXFP8 shard with Zipf(1.2)-skewed rows over its 16 experts
+    "mx_shard_zipf": dict(idx=7, T=32768, d=4096, E=16, f=1536, k=1, dtype="mxfp8",
+                          routing="zipf", bwd=True, gate="uniform01"),
 }
 
 ZIPF_S = 1.2

@@ -262,6 +262,45 @@ struct MxKParams {
     int64_t n_rows;
 };
 
+// Weight-gradient tiles go to the XCDs as contiguous ranges, or dealt in runs
+// of kMxDealRun when contiguous ranges would load the XCDs unevenly: a tile
+// costs about its group's padded row count (its K) plus a fixed overhead
+// worth some 256 rows, and uneven means the busiest XCD's share exceeds the
+// mean by more than 5%.  One wave decides ahead of each launch and leaves the
+// answer in g_mx_k_deal; either mapping covers every tile once, so launches
+// that overlap on one device can only make each other slower.
+constexpr int kMxDealRun = 4;
+__device__ int g_mx_k_deal;
+
+__global__ __launch_bounds__(64) void mx_k_deal_flag_kernel(MxKParams p, int tiles_e, int per_xcd)
+{
+    const int lane = threadIdx.x & 63;
+    float xc[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) xc[x] = 0.f;
+    for (int e = lane; e < p.E; e += 64) {
+        const int64_t m = group_rows(p.group_off, p.capacity, e, p.n_rows);
+        const float c = (float)((m + kMxColPad - 1) / kMxColPad * kMxColPad) + 256.f;
+        const int64_t a = (int64_t)e * tiles_e, b = a + tiles_e;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            const int64_t lo = max(a, (int64_t)x * per_xcd), hi = min(b, (int64_t)(x + 1) * per_xcd);
+            if (hi > lo) xc[x] += (float)(hi - lo) * c;
+        }
+    }
+    float mx = 0.f, sum = 0.f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+        float v = xc[x];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+        mx = fmaxf(mx, v);
+        sum += v;
+    }
+    // lanes may round the sums differently: lane 0 decides
+    if (threadIdx.x == 0) g_mx_k_deal = mx > 1.05f * (sum * 0.125f) ? 1 : 0;
+}
+
 template <int BM, int NW>
 __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void mx_grouped_k_kernel(MxKParams p)
 {
@@ -276,8 +315,8 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void mx_grouped_k_kernel(MxKParams p)
     const int per_xcd = (total + 7) / 8;
     const int xcd = blockIdx.x % 8;
     const int slot = blockIdx.x / 8;
-    if (slot >= per_xcd) return;
-    const int L = xcd * per_xcd + slot;
+    const int L = g_mx_k_deal ? ((slot / kMxDealRun) * 8 + xcd) * kMxDealRun + slot % kMxDealRun
+                              : (slot < per_xcd ? xcd * per_xcd + slot : total);
     if (L >= total) return;
     const int e = L / tiles_e;
     int local = L - e * tiles_e;
@@ -490,8 +529,13 @@ hipError_t gemm_op_mxfp8(int op, const moe_gemm_tensors& t, GroupSpec g, int d, 
     p1.ldc = d;
     p1.sC = (int64_t)2 * f * d;
     const int64_t total = (int64_t)g.E * (p0.mtn * p0.ntn + p1.mtn * p1.ntn);
-    const int64_t grid = (total + 7) / 8 * 8;
-    if (grid > 0) hipLaunchKernelGGL((mx_grouped_k_kernel<kMxBM, kMxNW>), dim3((unsigned)grid), dim3(64 * kMxNW), 0, s, k);
+    // whole runs of dealt tiles on each of the 8 XCDs
+    const int64_t grid = (total + 8 * kMxDealRun - 1) / (8 * kMxDealRun) * (8 * kMxDealRun);
+    if (grid > 0) {
+        hipLaunchKernelGGL(mx_k_deal_flag_kernel, dim3(1), dim3(64), 0, s, k,
+                           p0.mtn * p0.ntn + p1.mtn * p1.ntn, (int)((total + 7) / 8));
+        hipLaunchKernelGGL((mx_grouped_k_kernel<kMxBM, kMxNW>), dim3((unsigned)grid), dim3(64 * kMxNW), 0, s, k);
+    }
     return hipGetLastError();
 }
 

@@ -190,8 +190,33 @@ def _mx_oracle(inp, k, gate=None):
                                               (400, 128, 4, 128, 1, None), (1500, 256, 4, 256, 1, None)])
 def test_mx_layer_fwd_bwd(moe, T, d, E, f, k, empty):
     _say("mx-layer", T, d, E, f, k, "empty expert", empty)
+    _mx_layer_case(moe, T, d, E, f, k, empty)
+
+
+def test_mx_layer_skewed_groups(moe):
+    # Zipf(1.2) rows over 16 experts: contiguous weight-gradient tile ranges
+    # would load the XCDs unevenly, so the kernel deals its tiles (checked
+    # here on the CPU with the same cost model)
+    T, d, E, f, k = 1500, 256, 16, 128, 1
+    _say("mx-layer-skewed", T, d, E, f, k)
+    logits = moe_synth.router_logits(T, E, seed=41, routing="zipf")
+    counts = np.bincount(oracle.route(logits.numpy(), k)["topk_idx"].reshape(-1), minlength=E)
+    tiles_e = 2 * ((d + 255) // 256) * ((f + 255) // 256)
+    per = (E * tiles_e + 7) // 8
+    xc = np.zeros(8)
+    for e in range(E):
+        c = -(-counts[e] // 128) * 128 + 256.0
+        for x in range(8):
+            xc[x] += max(0, min((e + 1) * tiles_e, (x + 1) * per) - max(e * tiles_e, x * per)) * c
+    assert xc.max() > 1.05 * xc.mean(), "the case exercises the dealt tile mapping"
+    _mx_layer_case(moe, T, d, E, f, k, None, logits=logits)
+
+
+def _mx_layer_case(moe, T, d, E, f, k, empty, logits=None):
     from routing_grouped_gemm_amd.layer import MoELayer
     inp = moe_synth.make_inputs(T=T, d=d, E=E, f=f, k=k, seed=T + E)
+    if logits is not None:
+        inp["logits"] = logits
     if empty is not None:   # an expert no token picks: a zero-row group in every GEMM
         inp["logits"][:, empty] = -1e4
     inp["w13"] = (inp["w13"].float() * 3).to(torch.bfloat16)
