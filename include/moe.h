@@ -34,11 +34,11 @@
  *     device int32, may be NULL) with the MOE_ERR_* bits; the kernels then
  *     skip the offending element and finish normally.
  *   - Calls are re-entrant; results are bitwise reproducible for identical
- *     inputs (no floating-point atomics anywhere).  The one piece of library
- *     state is a device int per GPU that the bf16 weight-gradient GEMM writes
- *     just before its launch (how its tiles go to the XCDs); weight-gradient
- *     calls that overlap on one GPU may take each other's choice, which can
- *     change their speed but never their results.
+ *     inputs (no floating-point atomics anywhere).  The only library state
+ *     is one device int per GPU for each weight-gradient GEMM (bf16, MXFP8),
+ *     written just before its launch (how its tiles go to the XCDs);
+ *     weight-gradient calls that overlap on one GPU may take each other's
+ *     choice, which can change their speed but never their results.
  *   - Limits: 1 <= E <= 1024, 1 <= k <= min(E, 8), row widths d and f
  *     multiples of 8 (MXFP8: 32 for the permute / quantiser, 128 for the
  *     grouped GEMMs), all pointers 16-byte aligned, n_rows < 2^31.
