@@ -10,11 +10,14 @@ What each function computes, and the page passage it follows, is stated in
 
 Parity status: every function is pinned in ``tests/test_oracle_*.py``
 against brute force, library routines (torch / numpy), closed forms or
-invariants.  The MXFP8 scale-rounding direction (ceil of log2(amax/448)) is
-the reading of the tutorial's MXFP8 paragraph; it is pinned against that
-passage's stated property (block maximum never overflows 448) and torch's
-E4M3FN/E8M0 codecs, but its agreement with the pages' own implementation is
-parity unpinned.
+invariants; the MXFP8 composition of the FFN (``mx_h``, ``mx_dgu``, the
+substituted operands and the ``mx_qdq_*`` wrappers) against an independent
+torch float64 chain and exact operand probes, with planted mistakes in the
+C source that the checks catch (``tests/test_oracle_mx_chain.py``).  The
+MXFP8 scale-rounding direction (ceil of log2(amax/448)) is pinned against
+the property the tutorial's MXFP8 paragraph states (the block maximum never
+overflows 448, and the next smaller power of two would) and torch's
+E4M3FN/E8M0 codecs; the pages print no implementation to compare beyond that.
 """
 import ctypes
 import os
@@ -48,7 +51,16 @@ def _load():
         return _lib
     if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    _lib = open_library(_LIB_PATH)
+    return _lib
+
+
+def open_library(path):
+    """Open a compiled oracle library at `path` with every entry point's
+    argument types declared (the wrappers below call whichever library
+    ``_load`` returns; the tests open deliberately broken builds this way to
+    show their checks catch them)."""
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I, L, D = ctypes.c_int, ctypes.c_long, ctypes.c_double
     lib.oracle_round.argtypes = [D, I]
@@ -73,7 +85,6 @@ def _load():
     lib.oracle_mx_scale_exp.restype = I
     lib.oracle_mx_quantize_vector.argtypes = [P, L, L, P, L, P]
     lib.oracle_mx_qdq_vector.argtypes = [P, L, L, P, L]
-    _lib = lib
     return lib
 
 

@@ -34,10 +34,14 @@
  *
  * Parity pins: every function here is checked in tests/ against something
  * other than itself (brute force, library routines, closed forms,
- * invariants).  The MXFP8 scale-rounding direction (ceil) follows the
- * tutorial's MXFP8 paragraph; its agreement with the pages' own
- * implementation is parity unpinned (that implementation is not public
- * on the pages).
+ * invariants), the MXFP8 composition of the FFN (mx_h, mx_dgu and the
+ * substituted GEMM operands) against an independent torch chain and exact
+ * operand probes, with planted mistakes that the checks must catch.  The
+ * MXFP8 scale rounds the block maximum over 448 up to a power of two: of
+ * the two power-of-two roundings it is the one that keeps the block maximum
+ * from overflowing, the property the tutorial's MXFP8 paragraph states
+ * (pinned); the pages do not print their own code, so agreement with it
+ * cannot be checked beyond that property.
  */
 #include <math.h>
 #include <stdint.h>
