@@ -33,12 +33,11 @@
  *     index outside the destination) are OR-ed into *dev_err (a caller-owned
  *     device int32, may be NULL) with the MOE_ERR_* bits; the kernels then
  *     skip the offending element and finish normally.
- *   - Calls are re-entrant; results are bitwise reproducible for identical
- *     inputs (no floating-point atomics anywhere).  The only library state
- *     is one device int per GPU for each weight-gradient GEMM (bf16, MXFP8),
- *     written just before its launch (how its tiles go to the XCDs);
- *     weight-gradient calls that overlap on one GPU may take each other's
- *     choice, which can change their speed but never their results.
+ *   - Calls are re-entrant and keep no state between calls: everything a
+ *     call's kernels write goes to the caller's tensors and workspace, so
+ *     calls on different streams with different workspaces are independent.
+ *     Results are bitwise reproducible for identical inputs (no
+ *     floating-point atomics anywhere).
  *   - Limits: 1 <= E <= 1024, 1 <= k <= min(E, 8), row widths d and f
  *     multiples of 8 (MXFP8: 32 for the permute / quantiser, 128 for the
  *     grouped GEMMs), all pointers 16-byte aligned, n_rows < 2^31.
@@ -136,7 +135,12 @@ MOE_API int moe_permute(int dtype, const void* x, int T, int d, int k, const int
                 const int32_t* src_slot, const float* row_scale, int64_t n_rows,
                 void* x_perm, uint8_t* x_perm_scales, int32_t* dev_err, moe_stream_t stream);
 
-/* Bytes of scratch the grouped GEMM calls need (0 for MOE_F32 and MOE_BF16). */
+/* Bytes of scratch the grouped GEMM calls need: MOE_F32 none; MOE_BF16 the
+ * weight-gradient stage's control words (256 bytes: a small kernel ahead of
+ * that stage decides there how its tiles go to the XCDs); MOE_MXFP8 those
+ * plus the quantised operands of every stage.  A workspace is 16-byte
+ * aligned and used by one call at a time: calls that share one must run in
+ * order on one stream. */
 MOE_API size_t moe_gemm_workspace_bytes(int dtype, int E, int64_t n_rows, int d, int f);
 
 /*
@@ -185,6 +189,8 @@ MOE_API int moe_grouped_gemm_fwd(int dtype, const void* x_perm, const uint8_t* x
  * out  dgu        [n_rows, 2f]: [dg | du].
  * out  dx_perm    [n_rows, d].
  * out  dw13       [E, 2f, d], dw2 [E, d, f].
+ * in   ws         workspace of moe_gemm_workspace_bytes() bytes (MOE_BF16 and
+ *                 MOE_MXFP8; MOE_EWORKSPACE when missing or smaller).
  */
 MOE_API int moe_grouped_gemm_bwd(int dtype, const void* dy_perm, const void* x_perm,
                          const uint8_t* x_perm_scales, const void* gu, const void* h,
@@ -211,8 +217,9 @@ enum moe_gemm_op {
  * w13 / w2 (+ scales) hold the forward-direction caches for GATE_UP / DOWN
  * and the backward-direction caches for DGRAD_GATE_UP / DGRAD_DOWN; every
  * other activation is bf16; ws / ws_bytes is a workspace of at least
- * moe_gemm_workspace_bytes (every stage but GATE_UP writes into it, so
- * stages sharing one workspace must run in order on one stream). */
+ * moe_gemm_workspace_bytes, needed by every MXFP8 stage but GATE_UP and by
+ * the MOE_BF16 WGRAD stage (stages sharing one workspace must run in order
+ * on one stream). */
 typedef struct moe_gemm_tensors {
     const void* x_perm;          /* [n_rows, d]                     */
     const uint8_t* x_perm_scales;
@@ -281,7 +288,11 @@ MOE_API int moe_unpermute_combine(int dtype, const void* y_perm, const int32_t* 
  *                 scales[K * P_g / 32 ..) as [K][(P_{g+1} - P_g) / 32], where
  *                 P_g = sum over earlier groups of their row count rounded up
  *                 to 128.  The buffers must hold K * (rows + 128 * n_groups)
- *                 codes and 1/32 of that in scales.
+ *                 codes and 1/32 of that in scales.  K must be a multiple
+ *                 of 8 (16-byte source rows) and scales 4-byte aligned.
+ * Errors: MOE_EINVAL (sizes, null pointers, n_groups outside 1..1024),
+ * MOE_EALIGN (K, src / codes not 16-byte aligned, colwise scales not
+ * 4-byte aligned).
  */
 #define MOE_MX_COL_PAD 128
 MOE_API int moe_quantize_mxfp8(const void* src, int64_t rows, int K, int colwise,
@@ -289,8 +300,10 @@ MOE_API int moe_quantize_mxfp8(const void* src, int64_t rows, int K, int colwise
                        uint8_t* scales, moe_stream_t stream);
 
 /*
- * Shared experts (ungated experts every token also uses; several of them
- * equal one wider expert) as extra groups of the same grouped GEMM: from a
+ * Shared experts (the speed-read's training-recipe paragraph, the report's
+ * section on the model recipe: ungated experts every token also uses, whose
+ * merge with the routed output matters; several of them equal one wider
+ * expert) as extra groups of the same grouped GEMM: from a
  * route of k slots, the route of k + n_shared slots in which slot k + s of
  * token t is expert E + s with weight 1 and row R + s*T + t, after the R
  * routed rows (R = T*k, or E*C padded).  Then permute, the grouped GEMM

@@ -30,48 +30,23 @@
 
 #include "gemm_common.h"
 
-// ping-pong main loop for the grouped-M GEMMs with 256-row tiles and K a
-// multiple of 64 (0: the single-group loop everywhere)
-#ifndef MOE_GEMM_PINGPONG
-#define MOE_GEMM_PINGPONG 1
-#endif
-// the same loop for the weight-gradient GEMM (both operands MN-major, every
-// fragment two transposed LDS reads); measured about 5% slower there than the
-// single-group loop at 256 x 256 tiles over experts of ~512 rows
-// weight-gradient tiles dealt to the XCDs in runs of this many tiles when
-// contiguous ranges would load them unevenly (0: always contiguous).  A
-// weight-gradient tile's cost is its group's row count, so with uneven
-// groups (Zipf routing, shared experts) contiguous ranges leave one XCD with
-// the big groups: e128 under Zipf(1.2) 9.97 -> 2.97 ms, one shared expert
-// 5.86 -> 3.70 ms.  Dealt always, uniform e128 went 2.93 -> 2.97 ms with 2.9x
-// the HBM reads (each XCD's L2 then sees every expert), hence the test.
-// Runs of 16 measured the same, 32 slower.
-#ifndef MOE_GEMM_K_DEAL
-#define MOE_GEMM_K_DEAL 4
-#endif
-// single-group loop with both operands MN-major (the weight gradient): the
-// next k-slice's fragment reads go between the MFMAs instead of in a burst
-#ifndef MOE_GEMM_READ_INTERLEAVE
-#define MOE_GEMM_READ_INTERLEAVE 1
-#endif
-#ifndef MOE_GEMM_PINGPONG_K
-#define MOE_GEMM_PINGPONG_K 0
-#endif
-// 64- or 128-row tiles for the last M-tile of an expert when it has at most
-// 64 or 128 rows
-#ifndef MOE_GEMM_SMALL_TAIL
-#define MOE_GEMM_SMALL_TAIL 1
-#endif
-// the direct loads of the next K-step go out spread evenly over the first
-// LOAD_SPAN / 32 of a K-step's MFMAs (single-group loop)
-#ifndef MOE_GEMM_LOAD_SPAN
-#define MOE_GEMM_LOAD_SPAN 12
-#endif
-
 namespace moe {
 namespace {
 
 using namespace gemm;
+
+// Weight-gradient tiles are dealt to the XCDs in runs of this many tiles
+// when contiguous ranges would load the XCDs unevenly.  A weight-gradient
+// tile's cost is its group's row count, so with uneven groups (Zipf routing,
+// shared experts) contiguous ranges leave one XCD with the big groups (e128
+// under Zipf(1.2): 9.97 -> 2.97 ms, one shared expert 5.86 -> 3.70 ms).
+// Dealt always, uniform e128 went 2.93 -> 2.97 ms with 2.9x the HBM reads
+// (each XCD's L2 then sees every expert), hence the test ahead of each
+// launch.  Runs of 16 measured the same, 32 slower.
+constexpr int kKDealRun = 4;
+// The direct loads of the next K-step go out spread evenly over the first
+// kLoadSpan / 32 of a K-step's MFMAs (single-group loop; best of 8 .. 28).
+constexpr int kLoadSpan = 12;
 
 // One MFMA operand fragment (8 consecutive k of one row) for lane `lane`:
 // tile row row_base + (lane & 31), k = ks*16 + (lane >> 5)*8 + [0, 8).
@@ -128,7 +103,7 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
     constexpr int NB = LB::PER_WAVE;
     constexpr int NQ = NA + NB;                    // load instructions per wave per K-step
     constexpr int SM = MI * NJ;                    // MFMAs per k-slice
-    constexpr int SPAN = MOE_GEMM_LOAD_SPAN * KS * SM / 32 < NQ ? NQ : MOE_GEMM_LOAD_SPAN * KS * SM / 32;
+    constexpr int SPAN = kLoadSpan * KS * SM / 32 < NQ ? NQ : kLoadSpan * KS * SM / 32;
     static_assert(NS == 2, "two LDS stages");
     static_assert(KS >= 2 && KS % 2 == 0, "an even number of k-slices per K-step");
     static_assert(SPAN <= KS * SM, "the loads fit the K-step's MFMAs");
@@ -205,7 +180,7 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
                     }
             }
     };
-    constexpr bool RI = MOE_GEMM_READ_INTERLEAVE && A_MN && B_MN && MI * NJ >= MI + NJ;
+    constexpr bool RI = A_MN && B_MN && MI * NJ >= MI + NJ;
 
     // one K-step.  MODE 1: the next K-step lies inside K (or is masked past K
     // by the descriptors), so its loads go out without the K-tail test;
@@ -623,7 +598,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_m_kernel(MParams p)
         sb.rows1 = max(min(128, p.N - n0 - 128), 0);
     }
 
-    if constexpr (BM == 256 && MOE_GEMM_SMALL_TAIL) {
+    if constexpr (BM == 256) {
         // the last M-tile of an expert with at most 64 (128) rows: a 64-row
         // (128-row) tile, with a quarter (half) of the MFMAs and of the A
         // loads of a full tile
@@ -647,7 +622,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_m_kernel(MParams p)
         }
     }
     f32x16 acc[BM / 64][WL<NW>::NJ];
-    if constexpr (KAL && NW == 8 && BM == 256 && BK == 64 && MOE_GEMM_PINGPONG)
+    if constexpr (KAL && NW == 8 && BM == 256 && BK == 64)
         mainloop_pp<false, B_MN>(sa, sb, acc, smem);
     else
         mainloop<BM, BK, NS, false, B_MN, NW, KAL>(sa, sb, acc, smem);
@@ -674,6 +649,7 @@ struct KParams {
     const int32_t* group_off;
     int capacity, E;
     int64_t n_rows;
+    int* ctl;              // caller workspace: ctl[0] = tile mapping flag (k_deal_flag_kernel)
 };
 
 // Whether contiguous tile ranges would load the XCDs unevenly: a weight-gradient
@@ -710,17 +686,13 @@ __device__ __forceinline__ bool k_tiles_uneven(const KParams& p, int tiles_e, in
     return __builtin_amdgcn_readfirstlane(mx > 1.05f * (sum * 0.125f) ? 1 : 0) != 0;
 }
 
-// 1 if the weight-gradient tiles are dealt to the XCDs in runs, 0 for
-// contiguous ranges: written by k_deal_flag_kernel ahead of every
-// weight-gradient launch on the same stream.  Both mappings cover every tile
-// once, so launches that overlap on one device can at worst make each other
-// take the slower mapping, never a wrong result.
-__device__ int g_k_deal;
-
+// Writes p.ctl[0]: 1 if the weight-gradient tiles are dealt to the XCDs in
+// runs, 0 for contiguous ranges.  It runs ahead of every weight-gradient
+// launch on the same stream, and the flag lives in that call's workspace.
 __global__ __launch_bounds__(64) void k_deal_flag_kernel(KParams p, int tiles_e, int per_xcd)
 {
     const bool d = k_tiles_uneven(p, tiles_e, per_xcd);
-    if (threadIdx.x == 0) g_k_deal = d ? 1 : 0;
+    if (threadIdx.x == 0) p.ctl[0] = d ? 1 : 0;
 }
 
 // Grouped-K GEMM (weight gradients): C_e = A_e^T B_e over the rows of group e,
@@ -738,32 +710,24 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_kernel(KParams p)
     const int per_xcd = (total + 7) / 8;
     // a contiguous range per XCD: its L2 serves a few groups' operands
     const int Lc = slot < per_xcd ? xcd * per_xcd + slot : total;
-#if MOE_GEMM_K_DEAL
-    // or runs of MOE_GEMM_K_DEAL tiles dealt round-robin to the XCDs, so that
+    // or runs of kKDealRun tiles dealt round-robin to the XCDs, so that
     // every group's tiles, whatever its row count (the K of its tiles), spread
     // over all XCDs, as the flag kernel decided.  The group bounds of both
     // candidate tiles are read with the flag (selected, not branched on, so
     // the loads stay together): one memory round trip, as for a fixed mapping.
-    constexpr int RUN = MOE_GEMM_K_DEAL;
+    constexpr int RUN = kKDealRun;
     const int Ld = ((slot / RUN) * 8 + xcd) * RUN + slot % RUN;
     const int ec = min(Lc, total - 1) / tiles_e, ed = min(Ld, total - 1) / tiles_e;
     const int64_t gc0 = group_begin(p.group_off, p.capacity, ec, p.n_rows);
     const int64_t gc1 = group_begin(p.group_off, p.capacity, ec + 1, p.n_rows);
     const int64_t gd0 = group_begin(p.group_off, p.capacity, ed, p.n_rows);
     const int64_t gd1 = group_begin(p.group_off, p.capacity, ed + 1, p.n_rows);
-    const bool deal = g_k_deal != 0;
+    const bool deal = p.ctl[0] != 0;
     const int L = deal ? Ld : Lc;
     if (L >= total) return;
     const int e = L / tiles_e;
     const int64_t g0 = deal ? gd0 : gc0;
     const int m_e = (int)max((int64_t)0, deal ? gd1 - gd0 : gc1 - gc0);
-#else
-    const int L = Lc;
-    if (L >= total) return;
-    const int e = L / tiles_e;
-    const int64_t g0 = group_begin(p.group_off, p.capacity, e, p.n_rows);
-    const int m_e = (int)group_rows(p.group_off, p.capacity, e, p.n_rows);
-#endif
     int local = L - e * tiles_e;
     const int which = local < t0 ? 0 : 1;
     if (which) local -= t0;
@@ -784,11 +748,10 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_kernel(KParams p)
     sb.rows1 = 0;
     sb.K = m_e;
 
+    // (the ping-pong loop, with both operands transposed and 8 K-steps per
+    // tile, measured 5% slower here than the single-group loop)
     f32x16 acc[BM / 64][WL<NW>::NJ];
-    if constexpr (NW == 8 && BM == 256 && BK == 64 && MOE_GEMM_PINGPONG_K)
-        mainloop_pp<true, true>(sa, sb, acc, smem);
-    else
-        mainloop<BM, BK, NS, true, true, NW, true>(sa, sb, acc, smem);
+    mainloop<BM, BK, NS, true, true, NW, true>(sa, sb, acc, smem);
 
     if (q.Cf)
         add_tile_f32<BM, NW>(acc, q.Cf + (int64_t)e * q.sC + (int64_t)mt * BM * q.ldc, q.ldc, q.M - mt * BM,
@@ -809,15 +772,9 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_kernel(KParams p)
 // of 32 x 64, and staggering the workgroups' K order all measured slower).
 // The scores leave straight from the accumulators, four consecutive fp32
 // columns per lane.
-#ifndef MOE_ROUTER_WAVES
-#define MOE_ROUTER_WAVES 8
-#endif
-#ifndef MOE_ROUTER_STAGES
-#define MOE_ROUTER_STAGES 3
-#endif
-constexpr int kRM = 64, kRN = 128, kRK = 64, kRS = MOE_ROUTER_STAGES;
-constexpr int kRW = MOE_ROUTER_WAVES;   // 4: each wave 32 x 64; 8: 32 x 32 (two waves per SIMD)
-constexpr int kRJ = kRW == 8 ? 1 : 2;   // 32-expert blocks per wave
+constexpr int kRM = 64, kRN = 128, kRK = 64, kRS = 3;
+constexpr int kRW = 8;                  // waves: each 32 x 32 (two waves per SIMD)
+constexpr int kRJ = 1;                  // 32-expert blocks per wave
 
 __global__ __launch_bounds__(64 * kRW) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ w, int T, int E,
@@ -930,40 +887,19 @@ hipError_t launch_k(const KParams& p, hipStream_t s)
     int64_t tiles_e = 0;
     for (int i = 0; i < p.nprob; ++i) tiles_e += (int64_t)p.pr[i].mtn * p.pr[i].ntn;
     const int64_t total = (int64_t)p.E * tiles_e;
-#if MOE_GEMM_K_DEAL
     // whole runs on each of the 8 XCDs
-    const int64_t grid = (total + 8 * MOE_GEMM_K_DEAL - 1) / (8 * MOE_GEMM_K_DEAL) * (8 * MOE_GEMM_K_DEAL);
-#else
-    const int64_t grid = (total + 7) / 8 * 8;
-#endif
+    const int64_t grid = (total + 8 * kKDealRun - 1) / (8 * kKDealRun) * (8 * kKDealRun);
     if (grid == 0) return hipSuccess;
-#if MOE_GEMM_K_DEAL
     hipLaunchKernelGGL(k_deal_flag_kernel, dim3(1), dim3(64), 0, s, p, (int)tiles_e, (int)((total + 7) / 8));
-#endif
     hipLaunchKernelGGL((gemm_grouped_k_kernel<BM, BK, NS, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
     return hipGetLastError();
 }
 
-#ifndef MOE_GEMM_BM_M
-#define MOE_GEMM_BM_M 256
-#endif
-#ifndef MOE_GEMM_BM_K
-#define MOE_GEMM_BM_K 256
-#endif
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 64
-#endif
-#ifndef MOE_GEMM_NS
-#define MOE_GEMM_NS 2
-#endif
-constexpr int kBM = MOE_GEMM_BM_M;   // M tile of the grouped-M (forward / dgrad) GEMMs
-constexpr int kBMK = MOE_GEMM_BM_K;  // M tile of the grouped-K (weight gradient) GEMM
-constexpr int kBK = MOE_GEMM_BK;     // K step
-constexpr int kNS = MOE_GEMM_NS;     // LDS pipeline stages
-#ifndef MOE_GEMM_WAVES
-#define MOE_GEMM_WAVES 8
-#endif
-constexpr int kNW = MOE_GEMM_WAVES;  // waves per workgroup (4: one per SIMD, 8: two)
+constexpr int kBM = 256;   // M tile of the grouped-M (forward / dgrad) GEMMs
+constexpr int kBMK = 256;  // M tile of the grouped-K (weight gradient) GEMM
+constexpr int kBK = 64;    // K step
+constexpr int kNS = 2;     // LDS pipeline stages
+constexpr int kNW = 8;     // waves per workgroup (two per SIMD)
 
 }  // namespace
 
@@ -1044,6 +980,7 @@ hipError_t gemm_op_bf16(int op, const moe_gemm_tensors& t, GroupSpec g, int d, i
         k.capacity = g.capacity;
         k.E = g.E;
         k.n_rows = g.n_rows;
+        k.ctl = static_cast<int*>(t.ws);
         k.nprob = 2;
         KProblem& a = k.pr[0];
         a.A = (const uint16_t*)t.dy_perm;

@@ -260,6 +260,7 @@ struct MxKParams {
     const int32_t* group_off;
     int capacity, E;
     int64_t n_rows;
+    int* ctl;              // caller workspace: ctl[0] = tile mapping flag (mx_k_deal_flag_kernel)
 };
 
 // Weight-gradient tiles go to the XCDs as contiguous ranges, or dealt in runs
@@ -267,10 +268,8 @@ struct MxKParams {
 // costs about its group's padded row count (its K) plus a fixed overhead
 // worth some 256 rows, and uneven means the busiest XCD's share exceeds the
 // mean by more than 5%.  One wave decides ahead of each launch and leaves the
-// answer in g_mx_k_deal; either mapping covers every tile once, so launches
-// that overlap on one device can only make each other slower.
+// answer in the call's workspace (p.ctl[0]).
 constexpr int kMxDealRun = 4;
-__device__ int g_mx_k_deal;
 
 __global__ __launch_bounds__(64) void mx_k_deal_flag_kernel(MxKParams p, int tiles_e, int per_xcd)
 {
@@ -298,7 +297,7 @@ __global__ __launch_bounds__(64) void mx_k_deal_flag_kernel(MxKParams p, int til
         sum += v;
     }
     // lanes may round the sums differently: lane 0 decides
-    if (threadIdx.x == 0) g_mx_k_deal = mx > 1.05f * (sum * 0.125f) ? 1 : 0;
+    if (threadIdx.x == 0) p.ctl[0] = mx > 1.05f * (sum * 0.125f) ? 1 : 0;
 }
 
 template <int BM, int NW>
@@ -315,7 +314,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void mx_grouped_k_kernel(MxKParams p)
     const int per_xcd = (total + 7) / 8;
     const int xcd = blockIdx.x % 8;
     const int slot = blockIdx.x / 8;
-    const int L = g_mx_k_deal ? ((slot / kMxDealRun) * 8 + xcd) * kMxDealRun + slot % kMxDealRun
+    const int L = p.ctl[0] ? ((slot / kMxDealRun) * 8 + xcd) * kMxDealRun + slot % kMxDealRun
                               : (slot < per_xcd ? xcd * per_xcd + slot : total);
     if (L >= total) return;
     const int e = L / tiles_e;
@@ -357,15 +356,12 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void mx_grouped_k_kernel(MxKParams p)
 }
 
 constexpr int kMxBM = 256;
-// waves per workgroup of the MXFP8 GEMMs (4: one per SIMD, 8: two).  Eight
-// waves of 128 x 64 measured 1-2% faster over the MXFP8 shard's step than
-// four of 128 x 128 (down, both dgrads and the weight gradient 2-4% faster,
-// gate/up 2% slower); spreading the next K-step's direct loads between the
-// MFMAs, as the bf16 loop does, made it 10% slower here.
-#ifndef MOE_MX_WAVES
-#define MOE_MX_WAVES 8
-#endif
-constexpr int kMxNW = MOE_MX_WAVES;
+// waves per workgroup of the MXFP8 GEMMs: two per SIMD.  Eight waves of
+// 128 x 64 measured 1-2% faster over the MXFP8 shard's step than four of
+// 128 x 128 (down, both dgrads and the weight gradient 2-4% faster, gate/up
+// 2% slower); spreading the next K-step's direct loads between the MFMAs, as
+// the bf16 loop does, made it 10% slower here.
+constexpr int kMxNW = 8;
 
 template <int EPI>
 hipError_t launch_mx_m(const MxMParams& mp, hipStream_t s)
@@ -379,6 +375,7 @@ hipError_t launch_mx_m(const MxMParams& mp, hipStream_t s)
 
 // workspace carve-up (all offsets 256-byte aligned)
 struct MxWs {
+    int* ctl;                                             // kGemmCtlBytes of control words
     uint8_t *hq, *hs, *dyq, *dys, *dguq, *dgus;           // row-wise
     uint8_t *dyT, *dyTs, *hT, *hTs, *dguT, *dguTs, *xT, *xTs;   // column-wise, group-transposed
 };
@@ -392,7 +389,8 @@ size_t carve(void* ws, int E, int64_t R, int d, int f, MxWs* w)
                            (size_t)R * 2 * f, (size_t)R * 2 * f / 32, Rp * d, Rp * d / 32,
                            Rp * f, Rp * f / 32, Rp * 2 * f, Rp * 2 * f / 32, Rp * d, Rp * d / 32};
     uint8_t* base = reinterpret_cast<uint8_t*>(ws);
-    size_t off = 0;
+    if (w) w->ctl = reinterpret_cast<int*>(base);
+    size_t off = kGemmCtlBytes;
     uint8_t** dst[14] = {w ? &w->hq : nullptr, w ? &w->hs : nullptr, w ? &w->dyq : nullptr,
                          w ? &w->dys : nullptr, w ? &w->dguq : nullptr, w ? &w->dgus : nullptr,
                          w ? &w->dyT : nullptr, w ? &w->dyTs : nullptr, w ? &w->hT : nullptr,
@@ -504,6 +502,7 @@ hipError_t gemm_op_mxfp8(int op, const moe_gemm_tensors& t, GroupSpec g, int d, 
     k.capacity = g.capacity;
     k.E = g.E;
     k.n_rows = R;
+    k.ctl = w.ctl;
     MxKProblem& p0 = k.pr[0];   // dWd [d, f] = dy^T h
     p0.Aq = w.dyT;
     p0.As = w.dyTs;

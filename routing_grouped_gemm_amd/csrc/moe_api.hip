@@ -158,8 +158,9 @@ int moe_unpermute_combine(int dtype, const void* y_perm, const int32_t* dst_row,
 
 size_t moe_gemm_workspace_bytes(int dtype, int E, int64_t n_rows, int d, int f)
 {
-    if (dtype != MOE_MXFP8) return 0;
     if (E < 1 || n_rows < 0 || d < 1 || f < 1) return 0;
+    if (dtype == MOE_BF16) return kGemmCtlBytes;
+    if (dtype != MOE_MXFP8) return 0;
     return gemm_ws_mxfp8(E, n_rows, d, f);
 }
 
@@ -214,11 +215,10 @@ int moe_grouped_gemm_bwd(int dtype, const void* dy_perm, const void* x_perm,
     for (const void* p : {dy_perm, x_perm, gu, h, w13, w2, (const void*)dgu, (const void*)dx_perm,
                           (const void*)dw13, (const void*)dw2})
         if (!aligned16(p)) return MOE_EALIGN;
-    if (dtype == MOE_MXFP8) {
-        if (!x_perm_scales || !w13_scales || !w2_scales) return MOE_EINVAL;
-        if (!ws || ws_bytes < moe_gemm_workspace_bytes(dtype, E, n_rows, d, f) || !aligned16(ws))
-            return MOE_EWORKSPACE;
-    }
+    if (dtype == MOE_MXFP8 && (!x_perm_scales || !w13_scales || !w2_scales)) return MOE_EINVAL;
+    if (dtype != MOE_F32 &&
+        (!ws || ws_bytes < moe_gemm_workspace_bytes(dtype, E, n_rows, d, f) || !aligned16(ws)))
+        return MOE_EWORKSPACE;
     moe_gemm_tensors t{};
     t.x_perm = x_perm;
     t.x_perm_scales = x_perm_scales;
@@ -292,6 +292,10 @@ int moe_grouped_gemm_op(int op, int dtype, const moe_gemm_tensors* t,
             if (!aligned16(need[i])) return MOE_EALIGN;
         }
     }
+    // the bf16 weight gradient keeps its tile-mapping flag in the workspace
+    if (dtype == MOE_BF16 && op == MOE_GEMM_WGRAD &&
+        (!t->ws || t->ws_bytes < moe_gemm_workspace_bytes(dtype, E, n_rows, d, f) || !aligned16(t->ws)))
+        return MOE_EWORKSPACE;
     const GroupSpec g{capacity > 0 ? nullptr : group_off, capacity, E, n_rows};
     return run_gemm_op(op, dtype, *t, g, d, f, as_stream(stream));
 }
@@ -337,6 +341,8 @@ int moe_quantize_mxfp8(const void* src, int64_t rows, int K, int colwise, const 
         return status_of(launch_quantize_rows((const uint16_t*)src, rows, K, codes, scales, s));
     }
     if (group_off && (n_groups < 1 || n_groups > kMaxExperts)) return MOE_EINVAL;
+    // 16-byte loads along each source row; whole 32-bit scale words
+    if (K % 8 || (reinterpret_cast<uintptr_t>(scales) & 3u)) return MOE_EALIGN;
     return status_of(launch_quantize_cols((const uint16_t*)src, rows, K, group_off, 0,
                                           group_off ? n_groups : 1, codes, scales, s));
 }

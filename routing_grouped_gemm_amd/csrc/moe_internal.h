@@ -135,6 +135,9 @@ constexpr int kRouteTokensPerBlock = 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 8;
 constexpr int kMxColPad = 128;   // column-wise MXFP8 groups are padded to this many rows
+// Leading bytes of a grouped-GEMM workspace that hold the weight-gradient
+// launch's control words (written by a small kernel ahead of the launch).
+constexpr size_t kGemmCtlBytes = 256;
 
 inline hipStream_t as_stream(moe_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 

@@ -162,7 +162,7 @@ class MoELayer:
         of writing the bf16 dw13 / dw2.  Call after backward (it reads dgu)."""
         self._alloc_bwd()
         t = gemm_tensors(x_perm=self.x_perm, h=self.h, dy_perm=self.dy_perm, dgu=self.dgu,
-                         dw13_f32=dw13_f32, dw2_f32=dw2_f32)
+                         dw13_f32=dw13_f32, dw2_f32=dw2_f32, ws=self.gemm_ws)
         moe_grouped_gemm_op(MOE_GEMM_WGRAD, self.dtype, t, self.s_off, self.g_cap, self.G,
                             self.n_rows, self.d, self.f)
 
@@ -237,7 +237,7 @@ class MoELayer:
         else:
             moe_grouped_gemm_bwd(self.dtype, self.dy_perm, self.x_perm, self.gu, self.h,
                                  self.w13, self.w2, self.s_off, self.g_cap, self.dgu,
-                                 self.dx_perm, self.dw13, self.dw2)
+                                 self.dx_perm, self.dw13, self.dw2, ws=self.gemm_ws)
         moe_unpermute_combine(act_dt, self.dx_perm, self.s_dst, None, self.K, self.dx,
                               dev_err=self.dev_err)
         return self.dx, self.dw13, self.dw2

@@ -63,7 +63,9 @@ def test_route_workspace_formula(m):
     # lrank (T*k int32) + one histogram row of E int32 per 64 tokens, plus alignment slack
     assert a >= 16384 * 4 * 4 + 256 * 128 * 4
     assert a < 16384 * 4 * 4 + 256 * 128 * 4 + 1024
-    assert m.moe_gemm_workspace_bytes(m.MOE_BF16, 8, 1000, 128, 128) == 0
+    # bf16: only the weight gradient's control words; fp32: none
+    assert m.moe_gemm_workspace_bytes(m.MOE_BF16, 8, 1000, 128, 128) == 256
+    assert m.moe_gemm_workspace_bytes(m.MOE_F32, 8, 1000, 128, 128) == 0
 
 
 FAKE = 0x10000          # 16-byte aligned, never dereferenced (validation fails first)
@@ -137,6 +139,12 @@ def test_gemm_validation(m):
     assert fwd(dtype=m.MOE_MXFP8, xs=P, ws=None) == m.MOE_EWORKSPACE
     assert lib.moe_grouped_gemm_bwd(m.MOE_BF16, P, P, None, P, P, P, None, P, None, P, 0, 8, 100,
                                     128, 128, P, P, None, P, None, 0, None) == m.MOE_EINVAL
+    # the bf16 backward needs the (small) workspace of its weight-gradient stage
+    wsb16 = lib.moe_gemm_workspace_bytes(m.MOE_BF16, 8, 100, 128, 128)
+    assert wsb16 > 0 and lib.moe_gemm_workspace_bytes(m.MOE_F32, 8, 100, 128, 128) == 0
+    for ws, wsb in ((None, wsb16), (P, wsb16 - 1), (P + 4, wsb16)):
+        assert lib.moe_grouped_gemm_bwd(m.MOE_BF16, P, P, None, P, P, P, None, P, None, P, 0, 8, 100,
+                                        128, 128, P, P, P, P, ws, wsb, None) == m.MOE_EWORKSPACE
     # one MXFP8 stage: scales of the operands it reads, and the workspace for
     # every stage but GATE_UP (which reads only the dispatch payload and weights)
     t = m.MoeGemmTensors(**{n: P for n in m.GEMM_TENSOR_FIELDS})
@@ -155,6 +163,9 @@ def test_gemm_validation(m):
     assert lib.moe_quantize_mxfp8(P, 10, 48, 0, None, 0, P, P, None) == m.MOE_EALIGN
     assert lib.moe_quantize_mxfp8(P, -1, 64, 0, None, 0, P, P, None) == m.MOE_EINVAL
     assert lib.moe_quantize_mxfp8(P, 10, 64, 1, P, 0, P, P, None) == m.MOE_EINVAL
+    # column-wise: 16-byte source rows and whole scale words
+    assert lib.moe_quantize_mxfp8(P, 10, 60, 1, None, 0, P, P, None) == m.MOE_EALIGN
+    assert lib.moe_quantize_mxfp8(P, 10, 64, 1, None, 0, P, P + 2, None) == m.MOE_EALIGN
 
 
 def test_router_and_gate_grad_validation(m):
@@ -215,6 +226,8 @@ def test_wgrad_fp32_accumulate_validation(m):
     assert op(m.MOE_GEMM_WGRAD, dtype=m.MOE_F32) == m.MOE_EUNSUPPORTED
     t.dw13_f32, t.dw2_f32, t.dy_perm = P, P, None
     assert op(m.MOE_GEMM_WGRAD) == m.MOE_EINVAL               # operands still required
+    t.dy_perm, t.ws, t.ws_bytes = P, None, 0
+    assert op(m.MOE_GEMM_WGRAD) == m.MOE_EWORKSPACE           # the stage's control words
 
 
 def test_gemm_tensors_struct_matches_header(m, tmp_path):

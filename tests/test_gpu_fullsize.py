@@ -35,7 +35,8 @@ def _say(*a):
     sys.stdout.flush()
 
 
-CASES = [("e8", False), ("e128", False), ("e128_zipf", False), ("e128_zipf", True), ("e128_shared", False)]
+CASES = [("e8", False), ("e8_matched", False), ("e128", False), ("e128_zipf", False), ("e128_zipf", True),
+         ("e128_shared", False)]
 
 
 @pytest.fixture(scope="module")
@@ -55,6 +56,11 @@ def _run(m, name, padded):
     inp = moe_synth.make_inputs(name, device="cuda")
     lay = MoELayer(T, d, E, f, k, m.MOE_BF16, capacity=cap, n_shared=cfg.get("n_shared", 0))
     lay.set_weights(inp["w13"], inp["w2"])
+    # weight gradients start as NaN: a tile the weight-gradient GEMM never
+    # writes stays NaN and is found below over the whole tensors
+    lay._alloc_bwd()
+    lay.dw13.fill_(float("nan"))
+    lay.dw2.fill_(float("nan"))
     lay.forward(inp["logits"], inp["x"])
     lay.backward(inp["dout"])
     torch.cuda.synchronize()
@@ -79,6 +85,19 @@ def test_fullsize_layer(moe, name, padded):
     cfg, cap, inp, lay = _run(moe, name, padded)
     T, d, E, f, k = cfg["T"], cfg["d"], cfg["E"], cfg["f"], cfg["k"]
     assert int(lay.dev_err.item()) == 0
+    # every weight-gradient element written (the whole tensors, every expert)
+    assert bool(torch.isfinite(lay.dw13).all()) and bool(torch.isfinite(lay.dw2).all())
+    # fp32 accumulate-into from zero: the same tiles' sums added once, so
+    # rounding them to bf16 gives the bf16 weight gradients bit for bit (a
+    # tile skipped or added twice would not)
+    if not padded:
+        a13 = torch.zeros(lay.G, 2 * f, d, dtype=torch.float32, device="cuda")
+        a2 = torch.zeros(lay.G, d, f, dtype=torch.float32, device="cuda")
+        lay.wgrad_accumulate(a13, a2)
+        torch.cuda.synchronize()
+        assert torch.equal(a13.to(torch.bfloat16), lay.dw13), f"{name}: fp32-accumulated dW13"
+        assert torch.equal(a2.to(torch.bfloat16), lay.dw2), f"{name}: fp32-accumulated dW2"
+        del a13, a2
     # ---- routing, bit-exact over all tokens
     r = oracle.route(inp["logits"].cpu().numpy(), k, cap)
     np.testing.assert_array_equal(lay.topk_idx.cpu().numpy(), r["topk_idx"])
