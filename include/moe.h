@@ -114,6 +114,26 @@ MOE_API int moe_route_topk(const float* logits, int T, int E, int k, int capacit
                    void* ws, size_t ws_bytes, int32_t* dev_err, moe_stream_t stream);
 
 /*
+ * moe_route_topk for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same call and results, with the scratch taken from a fixed array the
+ * library holds on each GPU it runs on (MOE_ROUTE_NOALLOC_MAX_BYTES, 32 MiB,
+ * kept until the process ends) instead of a caller workspace.  It calls no
+ * allocator.  The current device must be the stream's device.  Returns
+ * MOE_EWORKSPACE when moe_route_workspace_bytes(T, E, k) exceeds the array
+ * (at E = 128, k = 4: T up to 1 398 080 tokens), MOE_EHIP if the array's
+ * device address cannot be looked up, otherwise as moe_route_topk.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a
+ * GPU (different streams or threads at once) race on it.  Nothing in the
+ * array needs clearing between calls (the route writes all of it it reads).
+ */
+#define MOE_ROUTE_NOALLOC_MAX_BYTES ((size_t)32 << 20)
+MOE_API int moe_route_topk_noalloc(const float* logits, int T, int E, int k, int capacity,
+                                   int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                                   int32_t* dst_row, int32_t* src_slot, int64_t n_rows,
+                                   int32_t* dev_err, moe_stream_t stream);
+
+/*
  * Rowwise dispatch (tutorial, "rowwise EP" paragraph): token row t is written
  * into row dst_row[t*k+j] of x_perm for every slot j with dst_row >= 0.
  *

@@ -21,7 +21,7 @@ MOE_ERR_NONFINITE_LOGIT, MOE_ERR_ROW_RANGE = 1, 2
 MOE_GEMM_GATE_UP, MOE_GEMM_DOWN, MOE_GEMM_DGRAD_DOWN, MOE_GEMM_DGRAD_GATE_UP, MOE_GEMM_WGRAD = \
     0, 1, 2, 3, 4
 
-ABI_FUNCTIONS = ("moe_route_workspace_bytes", "moe_route_topk", "moe_permute",
+ABI_FUNCTIONS = ("moe_route_workspace_bytes", "moe_route_topk", "moe_route_topk_noalloc", "moe_permute",
                  "moe_gemm_workspace_bytes", "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd",
                  "moe_grouped_gemm_op", "moe_unpermute_combine", "moe_quantize_mxfp8",
                  "moe_route_add_shared", "moe_router_logits", "moe_gate_grad", "moe_status_string",
@@ -67,6 +67,8 @@ def load():
     lib.moe_route_workspace_bytes.argtypes = [I, I, I]
     lib.moe_route_topk.restype = I
     lib.moe_route_topk.argtypes = [P, I, I, I, I, P, P, P, P, P, P, I64, P, SZ, P, P]
+    lib.moe_route_topk_noalloc.restype = I
+    lib.moe_route_topk_noalloc.argtypes = [P, I, I, I, I, P, P, P, P, P, P, I64, P, P]
     lib.moe_permute.restype = I
     lib.moe_permute.argtypes = [I, P, I, I, I, P, P, P, I64, P, P, P, P]
     lib.moe_gemm_workspace_bytes.restype = SZ
@@ -143,6 +145,20 @@ def moe_route_topk(logits, k, capacity, topk_idx, topk_w, counts, offsets, dst_r
                                _p(counts), _p(offsets), _p(dst_row), _p(src_slot), n_rows, _p(ws),
                                _nbytes(ws), _p(dev_err), _s(stream))
     _check(rc, "moe_route_topk")
+
+
+ROUTE_NOALLOC_MAX_BYTES = 32 << 20    # MOE_ROUTE_NOALLOC_MAX_BYTES in moe.h
+
+
+def moe_route_topk_noalloc(logits, k, capacity, topk_idx, topk_w, counts, offsets, dst_row, src_slot,
+                           dev_err=None, stream=None):
+    """moe_route_topk with the library's fixed per-GPU scratch instead of a workspace."""
+    T, E = logits.shape
+    n_rows = src_slot.numel()
+    rc = load().moe_route_topk_noalloc(_p(logits), T, E, k, capacity, _p(topk_idx), _p(topk_w),
+                                       _p(counts), _p(offsets), _p(dst_row), _p(src_slot), n_rows,
+                                       _p(dev_err), _s(stream))
+    _check(rc, "moe_route_topk_noalloc")
 
 
 def moe_permute(dtype, x, k, dst_row, x_perm, src_slot=None, row_scale=None, x_perm_scales=None,

@@ -1,6 +1,8 @@
 // C ABI entry points of libmoe: host-side argument validation, workspace
 // carving and kernel launches.  No entry point allocates, frees, copies to
 // the host or synchronises; everything is enqueued on the caller's stream.
+#include <mutex>
+
 #include "moe_internal.h"
 
 using namespace moe;
@@ -43,6 +45,37 @@ int run_gemm_op(int op, int dtype, const moe_gemm_tensors& t, const GroupSpec& g
     else if (dtype == MOE_BF16) e = gemm_op_bf16(op, t, g, d, f, s);
     else e = gemm_op_mxfp8(op, t, g, d, f, t.ws, s);
     return status_of(e);
+}
+
+// Scratch of moe_route_topk_noalloc: the route's per-pair ranks and per-block
+// histograms, for callers that cannot allocate.  A __device__ array exists
+// once per GPU, at that GPU's own address, from module load until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = MOE_ROUTE_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// device address of the current device's scratch array
+hipError_t scratch_of_current_device(void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+    *out = g_scratch_ptr[dev];
+    return *out ? hipSuccess : hipErrorInvalidSymbol;
 }
 
 }  // namespace
@@ -94,6 +127,18 @@ int moe_route_topk(const float* logits, int T, int E, int k, int capacity, int32
     return status_of(launch_route(logits, T, E, k, capacity, topk_idx, topk_w, counts, offsets,
                                   dst_row, src_slot, n_rows, lrank, hist, dev_err,
                                   as_stream(stream)));
+}
+
+int moe_route_topk_noalloc(const float* logits, int T, int E, int k, int capacity, int32_t* topk_idx,
+                           float* topk_w, int32_t* counts, int32_t* offsets, int32_t* dst_row,
+                           int32_t* src_slot, int64_t n_rows, int32_t* dev_err, moe_stream_t stream)
+{
+    // the route's scratch is written in full before it is read (every
+    // block's histogram row, every pair's rank), so nothing is cleared
+    void* ptr = nullptr;
+    if (scratch_of_current_device(&ptr) != hipSuccess) return MOE_EHIP;
+    return moe_route_topk(logits, T, E, k, capacity, topk_idx, topk_w, counts, offsets, dst_row, src_slot,
+                          n_rows, ptr, kNoAllocScratchBytes, dev_err, stream);
 }
 
 int moe_route_add_shared(int T, int E, int k, int n_shared, int capacity, const int32_t* topk_idx,
