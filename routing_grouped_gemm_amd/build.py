@@ -24,9 +24,17 @@ CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# per-file flags.  gemm_bf16.hip: one lane fetches the persistent weight-gradient
+# kernel's next tile position with a global atomic whose result is used only
+# after the tile's main loop; the compiler's atomic optimizer would turn it into
+# a wave-wide form that reads the result (and so waits for every outstanding
+# memory operation, the previous tile's output stores included) right away.
+EXTRA = {"gemm_bf16.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                      if "is not a recognized feature for this target" not in l)

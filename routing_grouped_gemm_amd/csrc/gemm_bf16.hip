@@ -89,9 +89,15 @@ __device__ __forceinline__ bf16x8 read_frag(const uint16_t* tile, int row_base, 
 // ks+1 are read while the MFMAs of slice ks run, and the MFMAs of each
 // K-step's last slice are issued after the next barrier, so that they cover
 // the latency of the first fragment reads of the new K-step.
-template <int BM, int BK, int NS, bool A_MN, bool B_MN, int NW, bool KAL>
+// PRE: K-step 0 was already issued into stage 0 by the caller (with loaders
+// made from the same sources); STORES16: the caller issued exactly 16 vector
+// memory operations per wave after those loads (and nothing else since), so
+// K-step 0 has landed once at most 16 are outstanding (vector memory
+// operations complete in issue order) and those may drain during K-step 0.
+template <int BM, int BK, int NS, bool A_MN, bool B_MN, int NW, bool KAL, bool PRE = false>
 __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
-                                         f32x16 (&acc)[BM / 64][WL<NW>::NJ], uint16_t* smem)
+                                         f32x16 (&acc)[BM / 64][WL<NW>::NJ], uint16_t* smem,
+                                         bool stores16 = false)
 {
     constexpr int MI = BM / 64;
     constexpr int NJ = WL<NW>::NJ;
@@ -126,8 +132,10 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
     LB lb;
     la.init(sa, lds_addr(smem));
     lb.init(sb, lds_addr(smem + BM * BK));
-    la.issue(smem, 0);
-    lb.issue(smem + BM * BK, 0);
+    if constexpr (!PRE) {
+        la.issue(smem, 0);
+        lb.issue(smem + BM * BK, 0);
+    }
 
     bf16x8 af[2][MI], bfr[2][NJ];
     auto read = [&](int buf, const uint16_t* a_s, const uint16_t* b_s, int ks) __attribute__((always_inline)) {
@@ -187,7 +195,9 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
     // 2: loads with the K-tail test, if there is a next K-step; 0: no loads
     auto kstep = [&](int kt, auto MODE) __attribute__((always_inline)) {
         constexpr int md = decltype(MODE)::value;
-        wait_vmcnt<0>();     // this wave's loads of K-step kt have landed
+        // this wave's loads of K-step kt have landed
+        if (PRE && kt == 0 && stores16) wait_vmcnt<16>();
+        else wait_vmcnt<0>();
         __syncthreads();     // everyone's have, and the other stage is no longer read
         const uint16_t* a_s = smem + (kt & 1) * STAGE;
         const uint16_t* b_s = a_s + BM * BK;
@@ -687,12 +697,15 @@ __device__ __forceinline__ bool k_tiles_uneven(const KParams& p, int tiles_e, in
 }
 
 // Writes p.ctl[0]: 1 if the weight-gradient tiles are dealt to the XCDs in
-// runs, 0 for contiguous ranges.  It runs ahead of every weight-gradient
-// launch on the same stream, and the flag lives in that call's workspace.
+// runs, 0 for contiguous ranges; and clears the per-XCD tile counters
+// p.ctl[1 .. 8] of the persistent kernel.  It runs ahead of every
+// weight-gradient launch on the same stream; both live in that call's
+// workspace.
 __global__ __launch_bounds__(64) void k_deal_flag_kernel(KParams p, int tiles_e, int per_xcd)
 {
     const bool d = k_tiles_uneven(p, tiles_e, per_xcd);
     if (threadIdx.x == 0) p.ctl[0] = d ? 1 : 0;
+    if (threadIdx.x >= 1 && threadIdx.x <= 8) p.ctl[threadIdx.x] = 0;
 }
 
 // Grouped-K GEMM (weight gradients): C_e = A_e^T B_e over the rows of group e,
@@ -759,6 +772,129 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_kernel(KParams p)
     else
         store_tile<BM, NW>(acc, q.C + (int64_t)e * q.sC + (int64_t)mt * BM * q.ldc, q.ldc, q.M - mt * BM,
                            nt * BN, q.N, reinterpret_cast<uint8_t*>(smem));
+}
+
+// Persistent weight-gradient GEMM, bf16 outputs.  One workgroup per CU walks
+// the tiles of its XCD's list (the contiguous range or the dealt runs the
+// flag kernel chose), taking positions from that XCD's counter in the
+// workspace, so tiles of very different K (their group's rows) still spread
+// evenly over the CUs.  Per tile, the same main loop and arithmetic as
+// gemm_grouped_k_kernel; between two tiles:
+//   - the next position is fetched while the current tile computes;
+//   - the next tile's first K-step goes out to LDS stage 0 before the current
+//     tile's epilogue, whose latency then hides under the epilogue;
+//   - the epilogue stages the result in stage 1, 128 rows at a time, and
+//     leaves through 16 buffer stores per wave that are always issued (out of
+//     range elements are dropped by the buffer's range), so the next tile's
+//     first wait is "at most 16 outstanding" and the stores drain while its
+//     first K-step computes, instead of every CU storing at once while none
+//     computes.
+template <int NW>
+__global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_persistent(KParams p)
+{
+    constexpr int BM = 256, BK = 64, NS = 2;
+    constexpr int STAGE = (BM + BN) * BK;           // elements per stage
+    __shared__ __align__(16) uint16_t smem[NS * STAGE];
+    __shared__ int s_pos[2];
+    const int t0 = p.pr[0].mtn * p.pr[0].ntn;
+    const int tiles_e = t0 + (p.nprob > 1 ? p.pr[1].mtn * p.pr[1].ntn : 0);
+    const int total = p.E * tiles_e;
+    const int xcd = blockIdx.x % 8;
+    const int per_xcd = (total + 7) / 8;
+    const bool deal = p.ctl[0] != 0;
+    int* counter = p.ctl + 1 + xcd;
+    // global tile at position j of this XCD's list, total past its end
+    auto tile_at = [&](int j) __attribute__((always_inline)) {
+        int L;
+        if (deal) L = ((j / kKDealRun) * 8 + xcd) * kKDealRun + j % kKDealRun;
+        else L = j < per_xcd ? xcd * per_xcd + j : total;
+        return __builtin_amdgcn_readfirstlane(L < total ? L : total);
+    };
+    // a tile, every field wave-uniform (kept in scalar registers)
+    struct KT {
+        int e, which, mt, nt, m_e;
+        int64_t g0;
+    };
+    auto uni64 = [](int64_t v) __attribute__((always_inline)) {
+        const uint64_t u = (uint64_t)v;
+        return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(u >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u));
+    };
+    auto describe = [&](int L, KT& t) __attribute__((always_inline)) {
+        t.e = L / tiles_e;
+        int local = L - t.e * tiles_e;
+        t.which = local < t0 ? 0 : 1;
+        if (t.which) local -= t0;
+        grouped_tile(local, t.which ? p.pr[1].mtn : p.pr[0].mtn, t.which ? p.pr[1].ntn : p.pr[0].ntn, 4,
+                     t.mt, t.nt);
+        t.mt = __builtin_amdgcn_readfirstlane(t.mt);
+        t.nt = __builtin_amdgcn_readfirstlane(t.nt);
+        const int64_t g0 = group_begin(p.group_off, p.capacity, t.e, p.n_rows);
+        const int64_t g1 = group_begin(p.group_off, p.capacity, t.e + 1, p.n_rows);
+        t.g0 = uni64(g0);
+        t.m_e = __builtin_amdgcn_readfirstlane((int)max((int64_t)0, g1 - g0));
+    };
+    auto sources = [&](const KT& t, TileSrc& sa, TileSrc& sb) __attribute__((always_inline)) {
+        const KProblem& q = t.which ? p.pr[1] : p.pr[0];
+        sa.p0 = sa.p1 = q.A + t.g0 * q.lda + (int64_t)t.mt * BM;
+        sa.ld = q.lda;
+        sa.rows0 = min(BM, q.M - t.mt * BM);
+        sa.rows1 = 0;
+        sa.K = t.m_e;
+        sb.p0 = sb.p1 = q.B + t.g0 * q.ldb + (int64_t)t.nt * BN;
+        sb.ld = q.ldb;
+        sb.rows0 = min(BN, q.N - t.nt * BN);
+        sb.rows1 = 0;
+        sb.K = t.m_e;
+    };
+    // K-step 0 of tile t into stage 0 (nothing for an empty group)
+    auto first_loads = [&](const KT& t) __attribute__((always_inline)) {
+        if (t.m_e == 0) return;
+        TileSrc sa, sb;
+        sources(t, sa, sb);
+        DirectLoader<BM, BK, true, NW> la;
+        DirectLoader<BN, BK, true, NW> lb;
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));    // recomputed here, not kept live across the tile loop
+        la.init_tid(sa, lds_addr(smem), tid);
+        lb.init_tid(sb, lds_addr(smem + BM * BK), tid);
+        la.issue(smem, 0);
+        lb.issue(smem + BM * BK, 0);
+    };
+
+    if (threadIdx.x == 0) s_pos[1] = atomicAdd(counter, 1);
+    __syncthreads();
+    int L = tile_at(s_pos[1]);
+    if (L >= total) return;
+    KT cur;
+    describe(L, cur);
+    first_loads(cur);
+    bool stores16 = false;
+    for (int it = 0;; ++it) {
+        int pos = 0;
+        if (threadIdx.x == 0) pos = atomicAdd(counter, 1);   // the next tile's position
+        TileSrc sa, sb;
+        sources(cur, sa, sb);
+        f32x16 acc[BM / 64][WL<NW>::NJ];
+        mainloop<BM, BK, NS, true, true, NW, true, true>(sa, sb, acc, smem, stores16);
+        if (threadIdx.x == 0) s_pos[it & 1] = pos;
+        __syncthreads();
+        const int Ln = tile_at(s_pos[it & 1]);
+        KT nxt = cur;
+        if (Ln < total) {
+            describe(Ln, nxt);
+            first_loads(nxt);
+        }
+        const KProblem& q = cur.which ? p.pr[1] : p.pr[0];
+        uint16_t* Ct = q.C + (int64_t)cur.e * q.sC + (int64_t)cur.mt * BM * q.ldc;
+        const int rows = q.M - cur.mt * BM;
+        uint8_t* stage1 = reinterpret_cast<uint8_t*>(smem + STAGE);
+        store_half_nt<NW>(acc, Ct, q.ldc, rows, cur.nt * BN, q.N, stage1, 0);
+        store_half_nt<NW>(acc, Ct, q.ldc, rows, cur.nt * BN, q.N, stage1, 1);
+        if (Ln >= total) return;
+        cur = nxt;
+        stores16 = true;
+    }
 }
 
 // Router scores: logits [T, E] fp32 = x [T, d] . W_r [E, d]^T, bf16 operands,
@@ -881,6 +1017,17 @@ hipError_t launch_m(const MParams& p, int64_t n_rows, hipStream_t s)
     return hipGetLastError();
 }
 
+// workgroups of a persistent launch: one per CU of the current device
+// (a multiple of 8, so that every XCD's tile list has workgroups)
+int persistent_grid()
+{
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 8)
+        ncu = 256;
+    return ncu / 8 * 8;
+}
+
 template <int BM, int BK, int NS, int NW>
 hipError_t launch_k(const KParams& p, hipStream_t s)
 {
@@ -891,7 +1038,16 @@ hipError_t launch_k(const KParams& p, hipStream_t s)
     const int64_t grid = (total + 8 * kKDealRun - 1) / (8 * kKDealRun) * (8 * kKDealRun);
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL(k_deal_flag_kernel, dim3(1), dim3(64), 0, s, p, (int)tiles_e, (int)((total + 7) / 8));
-    hipLaunchKernelGGL((gemm_grouped_k_kernel<BM, BK, NS, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
+    // the persistent kernel for bf16 outputs whose tile offsets fit its 31-bit buffer range
+    bool persistent = BM == 256 && BK == 64 && NS == 2 && NW == 8;
+    for (int i = 0; i < p.nprob; ++i)
+        persistent = persistent && !p.pr[i].Cf && (int64_t)256 * p.pr[i].ldc * 2 < ((int64_t)1 << 31);
+    if (persistent) {
+        const int64_t pgrid = std::min<int64_t>(persistent_grid(), (total + 7) / 8 * 8);
+        hipLaunchKernelGGL((gemm_grouped_k_persistent<NW>), dim3((unsigned)pgrid), dim3(64 * NW), 0, s, p);
+    } else {
+        hipLaunchKernelGGL((gemm_grouped_k_kernel<BM, BK, NS, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -131,10 +131,14 @@ struct DirectLoader {
             return (i * NW + w) * RPC_K >= HALF;
         }
     }
-    __device__ __forceinline__ void init(const TileSrc& s, uint32_t lds_tile = 0)
+    __device__ __forceinline__ void init(const TileSrc& s, uint32_t lds_tile = 0) { init_tid(s, lds_tile, threadIdx.x); }
+    // init with the thread index passed in (a caller inside a loop can pass a
+    // value the compiler cannot hoist, so the per-lane offsets are recomputed
+    // where they are needed instead of being kept live across the loop)
+    __device__ __forceinline__ void init_tid(const TileSrc& s, uint32_t lds_tile, int tid)
     {
-        const int lane = threadIdx.x & 63;
-        const int w = threadIdx.x >> 6;
+        const int lane = tid & 63;
+        const int w = tid >> 6;
         K = s.K;
         m0w = lds_tile + (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;
         if constexpr (!MN) {
@@ -597,6 +601,57 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[BM / 64][WL<NW>::
         const int n = col0 + 8 * c;
         if (r < rows && n < N) store16(C + r * ldc + n, v);
     });
+}
+
+// Rows [128 pass, 128 pass + 128) of a 256 x 256 accumulator tile (the
+// waves with wm == pass hold them) as bf16 rows of C: staged through the 64 KB
+// at lds, then 8 non-temporal 16-byte buffer stores per thread, always
+// issued: an element outside rows x (N - col0) gets an offset past the
+// buffer's range and the hardware drops it.  Ct is row 0, column 0 of the
+// tile (wave-uniform) and every in-range byte offset (row * ldc + col) * 2 is
+// below 2^31.  A barrier before the LDS reads and one after them.
+template <int NW>
+__device__ __forceinline__ void store_half_nt(const f32x16 (&acc)[4][WL<NW>::NJ], uint16_t* Ct, int64_t ldc,
+                                              int rows, int col0, int N, uint8_t* lds, int pass)
+{
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(Ct, (short)0, 0x7fffffff, 0x00020000);
+    constexpr int NT = WL<NW>::NT;
+    constexpr int PER = 128 * 32 / NT;            // 16-byte chunks per thread
+    // the thread index through an empty asm: the offsets below are then
+    // computed here rather than hoisted out of a caller's tile loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int wm = WL<NW>::wm(wave), wn = WL<NW>::wn(wave);
+    if (wm == pass) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < WL<NW>::NJ; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    stage_put(lds, stage_off<32>(i * 32 + (lane & 31), acc_col<NW>(wn, j, g, lane)),
+                              pack4_bf16(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                         acc[i][j][4 * g + 3]));
+    }
+    __syncthreads();
+    uint4 v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int q = tid + i * NT;
+        const int r = q >> 5, c = q & 31;
+        v[i] = *reinterpret_cast<const uint4*>(lds + r * 512 + ((c ^ (r & 31)) << 4));
+    }
+    typedef __attribute__((ext_vector_type(4))) uint32_t vu4;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int q = tid + i * NT;
+        const int r = 128 * pass + (q >> 5), n = col0 + 8 * (q & 31);
+        const uint32_t off = r < rows && n < N ? (uint32_t)((r * ldc + n) * 2) : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b128(vu4{v[i].x, v[i].y, v[i].z, v[i].w}, rsrc, (int)off, 0,
+                                               2 /* non-temporal */);
+    }
+    __syncthreads();
 }
 
 }  // namespace gemm
