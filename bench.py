@@ -233,38 +233,94 @@ def run_gpu(args, cfg):
     gpu_ms = sum(evs[i][0].elapsed_time(evs[i][len(STAGES)]) for i in range(K)) / K
     ms_per_step = wall * 1e3 / K
     counts = lay.counts.cpu()
-    graph = graph_replay(step, K, T)
+    cold = cold_cache(lay, inp, wts, act_dt, T, d, k, max(5, min(K, 10))) if dt != m.MOE_F32 and not S else None
     f1 = router_steps(lay, inp, K) if dt == m.MOE_BF16 and not cap else None
     f4 = wgrad_f32_accumulate(lay, K) if dt == m.MOE_BF16 and not cap else None
     wq = weight_requant(lay, K) if dt == m.MOE_MXFP8 else None
     return dict(stage_ms=stage_ms, gpu_ms=gpu_ms, ms_per_step=ms_per_step, R=R, cap=cap, f1=f1, wq=wq, f4=f4,
-                graph=graph,
+                cold=cold,
                 counts=counts, inp=inp, lay=lay)
 
 
-def graph_replay(step, reps, T):
-    """The same step captured once in a HIP graph and replayed `reps` times
-    (wall clock around the replays, synchronised on both sides): the launch
-    path without per-kernel host overhead.  Reported beside the eager step."""
+def cold_cache(lay, inp, wts, act_dt, T, d, k, reps):
+    """The HBM-bound stages timed one launch at a time with the caches cold:
+    before each repetition a 1 GiB buffer is written (more than the 256 MB
+    last-level cache and every L2 hold), so the stage's operands come from
+    HBM.  Median over `reps` launches of permute, combine, combine-backward
+    and permute-backward; bytes as in stage_work (each operand once)."""
     import torch
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step(None)
-    torch.cuda.current_stream().wait_stream(side)
+    import routing_grouped_gemm_amd as m
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    calls = {
+        "permute": lambda: lay.permute(inp["x"]),
+        "combine": lambda: lay.combine(wts),
+        "combine_bwd": lambda: m.moe_permute(act_dt, inp["dout"], lay.K, lay.s_dst, lay.dy_perm,
+                                             src_slot=lay.s_src, row_scale=wts, dev_err=lay.dev_err),
+        "permute_bwd": lambda: m.moe_unpermute_combine(act_dt, lay.dx_perm, lay.s_dst, None, lay.K, lay.dx,
+                                                       dev_err=lay.dev_err),
+    }
+    mx = lay.dtype == m.MOE_MXFP8
+    out = {}
+    for name, fn in calls.items():
+        ms = []
+        for _ in range(reps):
+            flush.fill_(1)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        ms.sort()
+        med = ms[len(ms) // 2]
+        _, by = stage_work(name, T, d, lay.E, lay.f, k, lay.n_rows if not lay.capacity else
+                           int((lay.dst_row >= 0).sum().item()), 2, mx and name == "permute")
+        out[name] = {"ms": round(med, 4), "gbs": round(by / med / 1e6, 1),
+                     "frac_hbm": round(by / med / 1e6 / PEAK_HBM_GBS, 4), "bytes": by}
+    del flush
+    return out
+
+
+def route_stress(reps, T=1 << 20, E=128, k=4):
+    """The route (top-k, histogram, scan, destination rows) alone at a large
+    token count, where its HBM traffic is big enough to measure: T = 2^20
+    tokens x E = 128 fp32 logits (537 MB), iid N(0, 1), top-4, each launch
+    bracketed by events; bytes as in stage_work('route')."""
+    import torch
+    import moe_synth
+    import routing_grouped_gemm_amd as m
+    logits = moe_synth.normal((T, E), 1.0, 4242, "cuda")
+    i32 = dict(dtype=torch.int32, device="cuda")
+    idx = torch.empty(T, k, **i32)
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, **i32)
+    offsets = torch.empty(E + 1, **i32)
+    dst = torch.empty(T * k, **i32)
+    src = torch.empty(T * k, **i32)
+    ws = torch.empty(m.moe_route_workspace_bytes(T, E, k), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, **i32)
+
+    def run():
+        m.moe_route_topk(logits, k, 0, idx, w, counts, offsets, dst, src, ws, dev_err=err)
+    run()
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step(None)
-    g.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    ms = []
     for _ in range(reps):
-        g.replay()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / reps
-    del g
-    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms / 1e3), 1)}
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    ms.sort()
+    med = ms[len(ms) // 2]
+    assert int(offsets[-1].item()) == T * k and int(err.item()) == 0
+    _, by = stage_work("route", T, 0, E, 0, k, T * k)
+    del logits, ws
+    return {"tokens": T, "experts": E, "top_k": k, "ms": round(med, 4), "gbs": round(by / med / 1e6, 1),
+            "frac_hbm": round(by / med / 1e6 / PEAK_HBM_GBS, 4), "bytes": by}
 
 
 def router_steps(lay, inp, reps):
@@ -493,13 +549,16 @@ def main():
         "roofline": rl,
         "expert_rows": {"min": int(res["counts"].min()), "max": int(res["counts"].max())},
     }
-    out["graph_replay"] = res["graph"]
     if res["f1"]:
         out["router_and_gate_grad"] = res["f1"]
     if res["wq"]:
         out["mx_weight_requant"] = res["wq"]
     if res["f4"]:
         out["wgrad_fp32_accumulate"] = res["f4"]
+    if res["cold"]:
+        out["hbm_stages_cold_cache"] = res["cold"]
+    if args.workload == "e128" and not args.padded:
+        out["route_stress"] = route_stress(max(5, min(args.steps, 10)))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, cfg, res["inp"])
     print(json.dumps(out), flush=True)

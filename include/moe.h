@@ -121,7 +121,7 @@ MOE_API int moe_route_topk(const float* logits, int T, int E, int k, int capacit
  * kept until the process ends) instead of a caller workspace.  It calls no
  * allocator.  The current device must be the stream's device.  Returns
  * MOE_EWORKSPACE when moe_route_workspace_bytes(T, E, k) exceeds the array
- * (at E = 128, k = 4: T up to 1 398 080 tokens), MOE_EHIP if the array's
+ * (at E = 128: T up to 4 194 240 tokens), MOE_EHIP if the array's
  * device address cannot be looked up, otherwise as moe_route_topk.
  * Every call on one GPU uses that GPU's one array: calls that overlap on a
  * GPU (different streams or threads at once) race on it.  Nothing in the

@@ -101,7 +101,8 @@ size_t moe_route_workspace_bytes(int T, int E, int k)
 {
     if (T < 0 || E < 1 || k < 1) return 0;
     const size_t nblk = ((size_t)T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock;
-    return align_up((size_t)T * k * sizeof(int32_t)) + align_up(nblk * E * sizeof(int32_t)) + kAlign;
+    (void)k;
+    return align_up(nblk * E * sizeof(int32_t)) + kAlign;
 }
 
 int moe_route_topk(const float* logits, int T, int E, int k, int capacity, int32_t* topk_idx,
@@ -119,13 +120,10 @@ int moe_route_topk(const float* logits, int T, int E, int k, int capacity, int32
     if (n_rows > 0 && !src_slot) return MOE_EINVAL;
     const size_t need = moe_route_workspace_bytes(T, E, k);
     if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
-    // carve: lrank [T*k], hist [nblk*E]
-    uint8_t* base = reinterpret_cast<uint8_t*>(
-        (reinterpret_cast<uintptr_t>(ws) + kAlign - 1) / kAlign * kAlign);
-    int32_t* lrank = reinterpret_cast<int32_t*>(base);
-    int32_t* hist = reinterpret_cast<int32_t*>(base + align_up((size_t)T * k * sizeof(int32_t)));
+    // the block histograms [E][nblk]
+    int32_t* hist = reinterpret_cast<int32_t*>((reinterpret_cast<uintptr_t>(ws) + kAlign - 1) / kAlign * kAlign);
     return status_of(launch_route(logits, T, E, k, capacity, topk_idx, topk_w, counts, offsets,
-                                  dst_row, src_slot, n_rows, lrank, hist, dev_err,
+                                  dst_row, src_slot, n_rows, hist, dev_err,
                                   as_stream(stream)));
 }
 
@@ -133,8 +131,8 @@ int moe_route_topk_noalloc(const float* logits, int T, int E, int k, int capacit
                            float* topk_w, int32_t* counts, int32_t* offsets, int32_t* dst_row,
                            int32_t* src_slot, int64_t n_rows, int32_t* dev_err, moe_stream_t stream)
 {
-    // the route's scratch is written in full before it is read (every
-    // block's histogram row, every pair's rank), so nothing is cleared
+    // the route's scratch (the block histograms) is written in full before it
+    // is read, so nothing is cleared
     void* ptr = nullptr;
     if (scratch_of_current_device(&ptr) != hipSuccess) return MOE_EHIP;
     return moe_route_topk(logits, T, E, k, capacity, topk_idx, topk_w, counts, offsets, dst_row, src_slot,

@@ -144,7 +144,7 @@ inline hipStream_t as_stream(moe_stream_t s) { return reinterpret_cast<hipStream
 // route
 hipError_t launch_route(const float* logits, int T, int E, int k, int capacity, int32_t* topk_idx,
                         float* topk_w, int32_t* counts, int32_t* offsets, int32_t* dst_row,
-                        int32_t* src_slot, int64_t n_rows, int32_t* lrank, int32_t* hist,
+                        int32_t* src_slot, int64_t n_rows, int32_t* hist,
                         int32_t* dev_err, hipStream_t stream);
 hipError_t launch_route_add_shared(const int32_t* idx_in, const float* w_in, const int32_t* dst_in,
                                    const int32_t* counts_in, const int32_t* offsets_in,

@@ -8,14 +8,18 @@
 //   1. route_topk_kernel: one segment of LPT lanes per token (16 logits per
 //      lane) selects the k largest fp32 logits by k rounds of a lane-local
 //      pass and a segmented butterfly arg-max (ties -> lower expert index),
-//      computes the softmax over the selected logits, and for its block of
-//      64 tokens the per-expert histogram (stored expert-major) and each
-//      pair's rank among the block's earlier pairs of the same expert.
-//   2. route_scan_kernel (one workgroup): prefix sums along each expert's
-//      row of block histograms (-> each block's base rank per expert),
-//      counts, and the exclusive scan of counts (-> offsets).
-//   3. route_finalize_kernel: dst_row = offsets[e] + base + local rank (or
-//      the padded row), src_slot as its inverse, padding rows -1.
+//      computes the softmax over the selected logits, and counts its block's
+//      64 tokens' pairs per expert (the block histogram, stored expert-major).
+//   2. route_scan_kernel (one workgroup per expert): exclusive prefix sums
+//      along each expert's row of block histograms (-> each block's first
+//      rank per expert) and the expert's count.
+//   3. route_finalize_kernel (one workgroup per block of 64 tokens): the
+//      expert offsets (exclusive scan of counts), then each pair's rank among
+//      its block's earlier pairs of the same expert -- found with a few wave
+//      ballots, one per bit of the expert index, that give each lane the
+//      mask of lanes holding its expert -- and dst_row = offsets[e] + block
+//      base + rank (or the padded row), src_slot as its inverse, padding rows
+//      -1.  The ranks are recomputed here rather than stored by kernel 1.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -25,14 +29,34 @@ namespace {
 
 constexpr int TB = kRouteTokensPerBlock;
 
-struct Cand {
-    float v;
-    int i;
-};
-
-__device__ __forceinline__ bool better(float v1, int i1, float v2, int i2)
+// maximum of a 64-bit value over aligned segments of L lanes (L a power of
+// two <= 64), every lane of a segment ending with it.  Within 16 lanes the
+// exchanges are DPP lane permutations (a maximum needs only some pairing per
+// step, not xor: quad swaps, then mirrored half-rows and rows); wider
+// segments exchange through ds_bpermute.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t x)
 {
-    return v1 > v2 || (v1 == v2 && i1 < i2);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+template <int L>
+__device__ __forceinline__ uint64_t segment_max(uint64_t x)
+{
+    auto mx = [](uint64_t a, uint64_t b) __attribute__((always_inline)) { return a > b ? a : b; };
+    if constexpr (L >= 2) x = mx(x, dpp64<0xB1>(x));     // quad_perm [1,0,3,2]
+    if constexpr (L >= 4) x = mx(x, dpp64<0x4E>(x));     // quad_perm [2,3,0,1]
+    if constexpr (L >= 8) x = mx(x, dpp64<0x141>(x));    // row_half_mirror
+    if constexpr (L >= 16) x = mx(x, dpp64<0x140>(x));   // row_mirror
+#pragma unroll
+    for (int off = 16; off < L; off <<= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, off, 64);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), off, 64);
+        x = mx(x, ((uint64_t)hi << 32) | lo);
+    }
+    return x;
 }
 
 // LPT lanes per token (power of two, <= 64); lane l of a token's segment owns
@@ -44,7 +68,6 @@ __global__ __launch_bounds__(NTHR) void route_topk_kernel(const float* __restric
                                                          int E, int k, int nblk,
                                                          int32_t* __restrict__ topk_idx,
                                                          float* __restrict__ topk_w,
-                                                         int32_t* __restrict__ lrank,
                                                          int32_t* __restrict__ hist,
                                                          int32_t* __restrict__ dev_err)
 {
@@ -84,41 +107,39 @@ __global__ __launch_bounds__(NTHR) void route_topk_kernel(const float* __restric
             for (int s = 0; s < VPL; ++s)
                 v[s] = active && e0 + s < E ? logits[(int64_t)t * E + e0 + s] : -INFINITY;
         }
+        // one 64-bit key per logit: the high word orders the fp32 values as
+        // unsigned integers (-0 taken as +0, non-finite as -inf), the low
+        // word is ~e, so a larger key is a larger logit or, for equal
+        // logits, a lower expert index.  Logits past E get key 0, below
+        // every real one.
+        uint64_t key[VPL];
 #pragma unroll
         for (int s = 0; s < VPL; ++s) {
-            if (active && e0 + s < E && !__builtin_isfinite(v[s])) bad = true;
-            if (!__builtin_isfinite(v[s])) v[s] = -INFINITY;
+            const bool in = e0 + s < E;
+            float x = v[s];
+            if (active && in && !__builtin_isfinite(x)) bad = true;
+            x = __builtin_isfinite(x) ? x : -INFINITY;
+            uint32_t u = __float_as_uint(x);
+            u = (u << 1) == 0 ? 0u : u;                       // -0 -> +0
+            const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+            key[s] = in ? ((uint64_t)ord << 32) | (uint32_t)~(uint32_t)(e0 + s) : 0ull;
         }
-        uint32_t taken = 0;
+        // k rounds: each lane's best key below the previous winner, then the
+        // segment's maximum (keys are distinct, so nothing is taken twice)
+        uint64_t thr = ~0ull;
         float sel_v[kMaxTopK];
         int sel_i[kMaxTopK];
 #pragma unroll
         for (int j = 0; j < kMaxTopK; ++j) {
             if (j < k) {
-                // lane-local best among not-taken valid entries
-                float bv = -INFINITY;
-                int bi = 0x7fffffff;
+                uint64_t best = 0;
 #pragma unroll
-                for (int s = 0; s < VPL; ++s) {
-                    const int e = e0 + s;
-                    if (e < E && !(taken & (1u << s)) && better(v[s], e, bv, bi)) {
-                        bv = v[s];
-                        bi = e;
-                    }
-                }
-                // segmented butterfly arg-max
-#pragma unroll
-                for (int off = LPT / 2; off > 0; off >>= 1) {
-                    const float ov = __shfl_xor(bv, off, 64);
-                    const int oi = __shfl_xor(bi, off, 64);
-                    if (better(ov, oi, bv, bi)) {
-                        bv = ov;
-                        bi = oi;
-                    }
-                }
-                if (bi / VPL == lane) taken |= 1u << (bi % VPL);
-                sel_v[j] = bv;
-                sel_i[j] = bi;
+                for (int s = 0; s < VPL; ++s) best = ((key[s] < thr) & (key[s] > best)) ? key[s] : best;
+                best = segment_max<LPT>(best);
+                thr = best;
+                const uint32_t hi = (uint32_t)(best >> 32);
+                sel_v[j] = __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
+                sel_i[j] = (int)~(uint32_t)best;
             }
         }
         if (active && lane == 0) {
@@ -147,65 +168,70 @@ __global__ __launch_bounds__(NTHR) void route_topk_kernel(const float* __restric
     if (bad && dev_err) atomicOr(dev_err, (int)MOE_ERR_NONFINITE_LOGIT);
     __syncthreads();
 
-    // rank of each pair among the block's earlier pairs of the same expert
+    // the block's pairs per expert
     const int P = nt * k;
-    for (int p = tid; p < P; p += NTHR) {
-        const int e = s_exp[p];
-        int r = 0;
-        for (int q = 0; q < p; ++q) r += (s_exp[q] == e);
-        lrank[(int64_t)t0 * k + p] = r;
-        atomicAdd(&s_hist[e], 1);  // integer count: order-independent
-    }
+    for (int p = tid; p < P; p += NTHR) atomicAdd(&s_hist[s_exp[p]], 1);  // integer count: order-independent
     __syncthreads();
     // expert-major: hist[e][block]
     for (int e = tid; e < E; e += NTHR) hist[(int64_t)e * nblk + blockIdx.x] = s_hist[e];
 }
 
-// One wave per expert: hist [E, nblk] (expert-major) is replaced by its
-// exclusive prefix along each expert's row (the first rank of each block
-// per expert) and counts[e] is the row total.  Each lane takes 8 consecutive
-// blocks per chunk of 512, all loads of a chunk in flight together.
+// One workgroup of 256 threads per expert: hist [E, nblk] (expert-major) is
+// replaced by its exclusive prefix along each expert's row (the first rank
+// of each block per expert) and counts[e] is the row total.  Per chunk of
+// 256 * SCH blocks each thread sums SCH consecutive entries (all loads in
+// flight together), the wave sums are scanned through LDS, and the chunk's
+// total carries into the next.
+constexpr int SCH = 16;
 __global__ __launch_bounds__(256) void route_scan_kernel(int32_t* __restrict__ hist, int nblk,
                                                          int E, int32_t* __restrict__ counts)
 {
-    constexpr int CH = 8;
-    const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= E) return;
+    __shared__ int s_w[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int e = blockIdx.x;
     int32_t* row = hist + (int64_t)e * nblk;
     int carry = 0;
-    for (int c0 = 0; c0 < nblk; c0 += 64 * CH) {
-        const int b0 = c0 + lane * CH;
-        int v[CH];
+    for (int c0 = 0; c0 < nblk; c0 += 256 * SCH) {
+        const int b0 = c0 + tid * SCH;
+        int v[SCH];
 #pragma unroll
-        for (int q = 0; q < CH; ++q) v[q] = b0 + q < nblk ? row[b0 + q] : 0;
+        for (int q = 0; q < SCH; ++q) v[q] = b0 + q < nblk ? row[b0 + q] : 0;
         int sum = 0;
 #pragma unroll
-        for (int q = 0; q < CH; ++q) sum += v[q];
-        // wave inclusive scan of the lane sums
+        for (int q = 0; q < SCH; ++q) sum += v[q];
         int incl = sum;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const int o = __shfl_up(incl, off, 64);
             if (lane >= off) incl += o;
         }
-        int run = carry + incl - sum;
+        if (lane == 63) s_w[wave] = incl;
+        __syncthreads();
+        int before = carry, chunk = 0;
 #pragma unroll
-        for (int q = 0; q < CH; ++q) {
+        for (int w = 0; w < 4; ++w) {
+            if (w < wave) before += s_w[w];
+            chunk += s_w[w];
+        }
+        int run = before + incl - sum;
+#pragma unroll
+        for (int q = 0; q < SCH; ++q) {
             if (b0 + q < nblk) row[b0 + q] = run;
             run += v[q];
         }
-        carry += __shfl(incl, 63, 64);
+        carry += chunk;
+        __syncthreads();   // s_w is rewritten by the next chunk
     }
-    if (lane == 0) counts[e] = carry;
+    if (tid == 0) counts[e] = carry;
 }
 
-// exclusive scan of counts[0..E) into s_off[0..E] by one block of 256 threads
+// exclusive scan of counts[0..E) into s_off[0..E] by one block of NT threads
+template <int NT>
 __device__ __forceinline__ void block_offsets(const int32_t* __restrict__ counts, int E, int* s_off,
                                               int* s_wsum)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    constexpr int PER = kMaxExperts / 256;   // 4 counts per thread
+    constexpr int PER = kMaxExperts / NT;    // counts per thread
     int v[PER], sum = 0;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
@@ -229,51 +255,79 @@ __device__ __forceinline__ void block_offsets(const int32_t* __restrict__ counts
         if (e < E) s_off[e] = run;
         run += v[q];
     }
-    if (tid == 255) s_off[E] = run;   // the last thread ends on the grand total
+    if (tid == NT - 1) s_off[E] = run;   // the last thread ends on the grand total
     __syncthreads();
 }
 
-// dst_row / src_slot of every pair; each block first forms the expert
-// offsets (exclusive scan of counts) in LDS, block 0 also stores them
-__global__ __launch_bounds__(256) void route_finalize_kernel(
-    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ lrank,
-    const int32_t* __restrict__ base, int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ counts, int T, int E, int k, int C, int nblk,
-    int32_t* __restrict__ dst_row, int32_t* __restrict__ src_slot, int64_t total)
+// One workgroup per block of TB tokens (FT threads: a wave per 64 pairs, all
+// of a block's TB * k <= 512 pairs at once).  The expert offsets come first
+// (exclusive scan of counts; block 0 stores them).  A pair's rank among its
+// block's earlier pairs of the same expert: lane l of wave w holds pair
+// 64 w + l; one ballot per bit of the expert index gives the mask of the
+// wave's lanes with the same expert, its population below l is the rank in
+// the wave, and the wave's per-expert counts (written by the first lane of
+// each expert) add the earlier waves' pairs.  Then
+// dst_row = offsets[e] + base[e][block] + rank (or e * C + rank when below
+// the capacity C, else -1) and src_slot[dst] = pair.  With C > 0 every row
+// of [e * C + counts[e], (e + 1) * C) gets src_slot -1 (grid-stride).
+constexpr int FT = TB * kMaxTopK;   // 512 threads
+__global__ __launch_bounds__(FT) void route_finalize_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ base, int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ counts, int T, int E, int k, int C, int nblk, int nbits,
+    int32_t* __restrict__ dst_row, int32_t* __restrict__ src_slot)
 {
+    constexpr int NWF = FT / 64;
     __shared__ int s_off[kMaxExperts + 1];
-    __shared__ int s_wsum[4];
-    block_offsets(counts, E, s_off, s_wsum);
+    __shared__ int s_wsum[NWF];
+    __shared__ int s_cnt[NWF][kMaxExperts];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int q = tid; q < NWF * kMaxExperts; q += FT) (&s_cnt[0][0])[q] = 0;
+    block_offsets<FT>(counts, E, s_off, s_wsum);   // (its barriers also order the clearing above)
     if (blockIdx.x == 0)
-        for (int e = threadIdx.x; e <= E; e += 256) offsets[e] = s_off[e];
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= total) return;
-    const int64_t P = (int64_t)T * k;
-    if (i < P) {
-        const int64_t t = i / k;
-        const int e = topk_idx[i];
-        const int rank = base[(int64_t)e * nblk + t / TB] + lrank[i];
+        for (int e = tid; e <= E; e += FT) offsets[e] = s_off[e];
+    const int b = blockIdx.x;
+    const int t0 = b * TB;
+    const int P = b < nblk ? min(TB, T - t0) * k : 0;
+    const int p = tid;                                   // this thread's pair of the block
+    const bool valid = p < P;
+    const int64_t i = (int64_t)t0 * k + p;
+    const int e = valid ? topk_idx[i] : 0;
+    // lanes of this wave with the same expert
+    uint64_t same = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+        const uint64_t on = __ballot(valid && ((e >> bit) & 1));
+        same &= ((e >> bit) & 1) ? on : ~on;
+    }
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int rank = __popcll(same & below);
+    // per-wave counts of the experts this wave holds (the first lane of each writes)
+    if (valid && rank == 0) s_cnt[wave][e] = __popcll(same);
+    __syncthreads();
+    if (valid) {
+        for (int w = 0; w < wave; ++w) rank += s_cnt[w][e];
+        rank += base[(int64_t)e * nblk + b];
         int64_t dst;
         if (C > 0) dst = rank < C ? (int64_t)e * C + rank : -1;
         else dst = (int64_t)s_off[e] + rank;
         dst_row[i] = (int32_t)dst;
         if (dst >= 0) src_slot[dst] = (int32_t)i;
     }
-    if (C > 0 && i < (int64_t)E * C) {
-        const int e = (int)(i / C);
-        const int r = (int)(i % C);
-        if (r >= counts[e]) src_slot[i] = -1;
+    if (C > 0) {
+        const int64_t rows = (int64_t)E * C;
+        for (int64_t r = (int64_t)b * FT + tid; r < rows; r += (int64_t)gridDim.x * FT) {
+            const int ee = (int)(r / C), rr = (int)(r % C);
+            if (rr >= counts[ee]) src_slot[r] = -1;
+        }
     }
 }
 
 template <int LPT, int VPL>
 void launch_topk(int nblk, hipStream_t s, const float* logits, int T, int E, int k,
-                 int32_t* topk_idx, float* topk_w, int32_t* lrank, int32_t* hist,
-                 int32_t* dev_err)
+                 int32_t* topk_idx, float* topk_w, int32_t* hist, int32_t* dev_err)
 {
     constexpr int NTHR = TB * LPT < 1024 ? (TB * LPT < 64 ? 64 : TB * LPT) : 1024;
     hipLaunchKernelGGL((route_topk_kernel<LPT, VPL, NTHR>), dim3(nblk), dim3(NTHR), 0, s, logits, T, E,
-                       k, nblk, topk_idx, topk_w, lrank, hist, dev_err);
+                       k, nblk, topk_idx, topk_w, hist, dev_err);
 }
 
 // Shared experts as extra groups: every token also takes slots k .. k+S-1,
@@ -341,32 +395,30 @@ hipError_t launch_route_add_shared(const int32_t* idx_in, const float* w_in, con
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int capacity, int32_t* topk_idx,
                         float* topk_w, int32_t* counts, int32_t* offsets, int32_t* dst_row,
-                        int32_t* src_slot, int64_t n_rows, int32_t* lrank, int32_t* hist,
-                        int32_t* dev_err, hipStream_t s)
+                        int32_t* src_slot, int64_t n_rows, int32_t* hist, int32_t* dev_err, hipStream_t s)
 {
+    (void)n_rows;
     const int nblk = (T + TB - 1) / TB;
     if (nblk > 0) {
         // 16 logits per lane (8 below 9 experts): a token's segment is E/16 lanes
-        if (E <= 8) launch_topk<1, 8>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
-        else if (E <= 16) launch_topk<1, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
-        else if (E <= 32) launch_topk<2, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
-        else if (E <= 64) launch_topk<4, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
-        else if (E <= 128) launch_topk<8, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
-        else if (E <= 256) launch_topk<16, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
-        else if (E <= 512) launch_topk<32, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
-        else launch_topk<64, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, lrank, hist, dev_err);
+        if (E <= 8) launch_topk<1, 8>(nblk, s, logits, T, E, k, topk_idx, topk_w, hist, dev_err);
+        else if (E <= 16) launch_topk<1, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, hist, dev_err);
+        else if (E <= 32) launch_topk<2, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, hist, dev_err);
+        else if (E <= 64) launch_topk<4, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, hist, dev_err);
+        else if (E <= 128) launch_topk<8, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, hist, dev_err);
+        else if (E <= 256) launch_topk<16, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, hist, dev_err);
+        else if (E <= 512) launch_topk<32, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, hist, dev_err);
+        else launch_topk<64, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, hist, dev_err);
     }
     // also for T = 0: the scan then writes zero counts
-    hipLaunchKernelGGL(route_scan_kernel, dim3((unsigned)((E + 3) / 4)), dim3(256), 0, s, hist, nblk, E,
-                       counts);
-    const int64_t P = (int64_t)T * k;
-    const int64_t total = capacity > 0 ? (P > n_rows ? P : n_rows) : P;
-    {   // at least one block: it stores the offsets
-        const int64_t grid = total > 0 ? (total + 255) / 256 : 1;
-        hipLaunchKernelGGL(route_finalize_kernel, dim3((unsigned)grid), dim3(256), 0, s, topk_idx,
-                           lrank, hist, offsets, counts, T, E, k, capacity, nblk, dst_row, src_slot,
-                           total);
-    }
+    hipLaunchKernelGGL(route_scan_kernel, dim3((unsigned)E), dim3(256), 0, s, hist, nblk, E, counts);
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    // at least one block: it stores the offsets; padded rows beyond the counts
+    // are covered grid-stride by however many blocks there are
+    const int grid = nblk > 0 ? nblk : 1;
+    hipLaunchKernelGGL(route_finalize_kernel, dim3((unsigned)grid), dim3(FT), 0, s, topk_idx, hist, offsets,
+                       counts, T, E, k, capacity, nblk, nbits, dst_row, src_slot);
     return hipGetLastError();
 }
 

@@ -60,9 +60,9 @@ def test_version_and_status_strings(m):
 def test_route_workspace_formula(m):
     assert m.moe_route_workspace_bytes(-1, 8, 2) == 0
     a = m.moe_route_workspace_bytes(16384, 128, 4)
-    # lrank (T*k int32) + one histogram row of E int32 per 64 tokens, plus alignment slack
-    assert a >= 16384 * 4 * 4 + 256 * 128 * 4
-    assert a < 16384 * 4 * 4 + 256 * 128 * 4 + 1024
+    # one histogram row of E int32 per 64 tokens, plus alignment slack
+    assert a >= 256 * 128 * 4
+    assert a < 256 * 128 * 4 + 1024
     # bf16: only the weight gradient's control words; fp32: none
     assert m.moe_gemm_workspace_bytes(m.MOE_BF16, 8, 1000, 128, 128) == 256
     assert m.moe_gemm_workspace_bytes(m.MOE_F32, 8, 1000, 128, 128) == 0

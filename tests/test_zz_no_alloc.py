@@ -77,7 +77,7 @@ def test_noalloc_route_size_limit(m):
     lib = m.load()
     E, k = 128, 4
     cap_bytes = m.ROUTE_NOALLOC_MAX_BYTES
-    T_max = 1398080                                       # moe.h: largest T at E = 128, k = 4
+    T_max = 4194240                                       # moe.h: largest T at E = 128
     assert lib.moe_route_workspace_bytes(T_max, E, k) <= cap_bytes
     assert lib.moe_route_workspace_bytes(T_max + 1, E, k) > cap_bytes
     fake = ctypes.c_void_p(0x10000)                        # never dereferenced: refused first
