@@ -237,9 +237,11 @@ enum moe_gemm_op {
  * w13 / w2 (+ scales) hold the forward-direction caches for GATE_UP / DOWN
  * and the backward-direction caches for DGRAD_GATE_UP / DGRAD_DOWN; every
  * other activation is bf16; ws / ws_bytes is a workspace of at least
- * moe_gemm_workspace_bytes, needed by every MXFP8 stage but GATE_UP and by
- * the MOE_BF16 WGRAD stage (stages sharing one workspace must run in order
- * on one stream). */
+ * moe_gemm_workspace_bytes, needed by every MXFP8 stage and by the MOE_BF16
+ * WGRAD stage.  MXFP8 stages hand operands on through it: GATE_UP leaves the
+ * row-wise MXFP8 copy of h that DOWN reads, DGRAD_DOWN the copy of dgu that
+ * DGRAD_GATE_UP reads, so those pairs run in order on one stream with one
+ * workspace and the h / dgu they see are the ones those epilogues wrote. */
 typedef struct moe_gemm_tensors {
     const void* x_perm;          /* [n_rows, d]                     */
     const uint8_t* x_perm_scales;

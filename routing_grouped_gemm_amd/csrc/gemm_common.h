@@ -278,7 +278,65 @@ struct MParams {
     const uint16_t* G;     // SWIGLU_BWD: saved gu
     int64_t ldg;
     int f;                 // SWIGLU: column offset of the u half in gu / dgu
+    // optional (MXFP8 stages): the row-wise MXFP8 copy of h (SWIGLU_FWD) or
+    // of dgu (SWIGLU_BWD), codes [rows, ldq] and E8M0 scales [rows, ldq / 32],
+    // made from the bf16 values the epilogue stores
+    uint8_t* Mq;
+    uint8_t* Ms;
+    int64_t ldq;
 };
+
+// Row-wise MXFP8 of 32 bf16 held as 8 by each of four consecutive lanes
+// (lanes 4j .. 4j+3, in element order): the block maximum and finiteness are
+// combined across the quad with DPP lane exchanges, then each lane encodes its
+// 8 elements -- the same arithmetic as the standalone quantiser (scale rule,
+// hardware round-to-nearest-even conversion for finite blocks, the software
+// encoder for blocks with a NaN or an infinity).  All four lanes must execute
+// it.  Returns the scale exponent; codes in element order, byte b of word w
+// = element 4w + b.
+__device__ __forceinline__ int mx_quant8_quad(uint4 v, uint2& codes)
+{
+    float x[8];
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        x[2 * p] = bf16_lo(wv[p]);
+        x[2 * p + 1] = bf16_hi(wv[p]);
+    }
+    float amax = 0.0f;
+    int finite = 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float a = fabsf(x[i]);
+        amax = fmaxf(amax, a);
+        finite &= a <= 3.402823466e38f ? 1 : 0;
+    }
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0xB1, 0xF, 0xF, false)));
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x4E, 0xF, 0xF, false)));
+    finite &= __builtin_amdgcn_update_dpp(0, finite, 0xB1, 0xF, 0xF, false);
+    finite &= __builtin_amdgcn_update_dpp(0, finite, 0x4E, 0xF, 0xF, false);
+    const int e = mx_scale_exp(amax);
+    uint32_t w[2];
+    if (finite) {
+#pragma unroll
+        for (int wi = 0; wi < 2; ++wi) {
+            const float q0 = __builtin_ldexpf(x[wi * 4 + 0], -e), q1 = __builtin_ldexpf(x[wi * 4 + 1], -e);
+            const float q2 = __builtin_ldexpf(x[wi * 4 + 2], -e), q3 = __builtin_ldexpf(x[wi * 4 + 3], -e);
+            const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+            w[wi] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, lo, true);
+        }
+    } else {
+#pragma unroll
+        for (int wi = 0; wi < 2; ++wi) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) word |= f32_to_e4m3(__builtin_ldexpf(x[wi * 4 + b], -e)) << (8 * b);
+            w[wi] = word;
+        }
+    }
+    codes = make_uint2(w[0], w[1]);
+    return e;
+}
 
 // Epilogues stage the bf16 result tile in LDS (free once the main loop has
 // ended) and store it row by row: each lane writes 16 contiguous bytes and a
@@ -348,7 +406,9 @@ __device__ __forceinline__ void stage_acc(const f32x16 (&acc)[BM / 64][WL<NW>::N
                                      acc[i][j][4 * g + 3]));
 }
 
-template <int BM, int EPI, int NW = 4>
+// MXQ: the SwiGLU epilogues also write the row-wise MXFP8 copy of their
+// bf16 output (h or dgu) to p.Mq / p.Ms
+template <int BM, int EPI, int NW = 4, bool MXQ = false>
 __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][WL<NW>::NJ], const MParams& p,
                                            int64_t row0, int rows_valid, int nt, uint8_t* lds)
 {
@@ -386,10 +446,24 @@ __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][WL<NW>::
                     stage_put(lds, stage_off<16>(wm * (BM / 2) + i * 32 + (lane & 31), acc_col<NW>(wn, j, g, lane)),
                               pack4_bf16(hv[0], hv[1], hv[2], hv[3]));
                 }
-        stage_flush<BM, 16, NT>(lds, [&](int r, int c, uint4 v) {
-            const int n = n0 + 8 * c;
-            if (r < rows_valid && n < p.f) *reinterpret_cast<uint4*>(p.H + (row0 + r) * p.ldh + n) = v;
-        });
+        if constexpr (MXQ) {
+            // h also leaves as row-wise MXFP8: the four lanes of each 32-column block encode it together
+            stage_flush<BM, 16, NT>(lds, [&](int r, int c, uint4 v) {
+                const int n = n0 + 8 * c;
+                uint2 q;
+                const int e = mx_quant8_quad(v, q);
+                if (r < rows_valid && n < p.f) {
+                    *reinterpret_cast<uint4*>(p.H + (row0 + r) * p.ldh + n) = v;
+                    *reinterpret_cast<uint2*>(p.Mq + (row0 + r) * p.ldq + n) = q;
+                    if ((c & 3) == 0) p.Ms[(row0 + r) * (p.ldq / 32) + n / 32] = (uint8_t)(e + 127);
+                }
+            });
+        } else {
+            stage_flush<BM, 16, NT>(lds, [&](int r, int c, uint4 v) {
+                const int n = n0 + 8 * c;
+                if (r < rows_valid && n < p.f) *reinterpret_cast<uint4*>(p.H + (row0 + r) * p.ldh + n) = v;
+            });
+        }
     } else {
         // SwiGLU backward, 128 tile columns at a time (accumulator sub-tiles
         // j = 2*ch, 2*ch+1 of every wave): the g and u tiles of those columns
@@ -401,8 +475,9 @@ __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][WL<NW>::
         uint8_t* lg = lds;
         uint8_t* lu = lds + QTILE;
         const desc_t g_desc = make_desc(p.G + row0 * p.ldg, (int64_t)rows_valid * p.ldg * 2);
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
+        // the two 128-column halves, each with its half index known at compile time
+        auto half = [&](auto CH_) __attribute__((always_inline)) {
+            constexpr int ch = decltype(CH_)::value;
             const int nc = n0 + 128 * ch;                   // first column of this half
 #pragma unroll
             for (int i = 0; i < QTILE / 1024 / NW; ++i) {
@@ -449,17 +524,38 @@ __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][WL<NW>::
                 const int r = qq >> 4, c = qq & 15;
                 v[i] = *reinterpret_cast<const uint4*>((which ? lu : lg) + r * 256 + ((c ^ (r & 15)) << 4));
             }
+            if constexpr (MXQ) {
+                // dgu also leaves as row-wise MXFP8 (32-column blocks never straddle dg | du)
 #pragma unroll
-            for (int i = 0; i < NQ; ++i) {
-                const int q = (int)threadIdx.x + i * NT;
-                const int which = q / (BM * 16), qq = q % (BM * 16);
-                const int r = qq >> 4, c = qq & 15;
-                const int n = nc + 8 * c;
-                if (r < rows_valid && n < p.N)
-                    *reinterpret_cast<uint4*>(p.C + (row0 + r) * p.ldc + (which ? p.f + n : n)) = v[i];
+                for (int i = 0; i < NQ; ++i) {
+                    const int q = (int)threadIdx.x + i * NT;
+                    const int which = q / (BM * 16), qq = q % (BM * 16);
+                    const int r = qq >> 4, c = qq & 15;
+                    const int n = nc + 8 * c;
+                    uint2 cq;
+                    const int e = mx_quant8_quad(v[i], cq);
+                    if (r < rows_valid && n < p.N) {
+                        const int col = which ? p.f + n : n;
+                        *reinterpret_cast<uint4*>(p.C + (row0 + r) * p.ldc + col) = v[i];
+                        *reinterpret_cast<uint2*>(p.Mq + (row0 + r) * p.ldq + col) = cq;
+                        if ((c & 3) == 0) p.Ms[(row0 + r) * (p.ldq / 32) + col / 32] = (uint8_t)(e + 127);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NQ; ++i) {
+                    const int q = (int)threadIdx.x + i * NT;
+                    const int which = q / (BM * 16), qq = q % (BM * 16);
+                    const int r = qq >> 4, c = qq & 15;
+                    const int n = nc + 8 * c;
+                    if (r < rows_valid && n < p.N)
+                        *reinterpret_cast<uint4*>(p.C + (row0 + r) * p.ldc + (which ? p.f + n : n)) = v[i];
+                }
             }
             __syncthreads();
-        }
+        };
+        half(std::integral_constant<int, 0>{});
+        half(std::integral_constant<int, 1>{});
     }
 }
 

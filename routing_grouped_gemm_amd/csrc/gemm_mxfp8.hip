@@ -7,9 +7,10 @@
 // dimension, with forward- and backward-direction weight caches.  Every GEMM
 // here therefore reads both operands with K contiguous:
 //   forward   gu = x Wg|Wu^T       x row-wise (dispatch payload), W13 forward cache
-//             y  = h Wd^T          h quantised row-wise here,     W2 forward cache
+//             y  = h Wd^T          h row-wise (made by the gate/up epilogue), W2 forward cache
 //   dgrad     dh = dy Wd           dy row-wise,  Wd^T  (backward cache [E, f, d])
-//             dx = dgu [Wg;Wu]     dgu row-wise, W13^T (backward cache [E, d, 2f])
+//             dx = dgu [Wg;Wu]     dgu row-wise (made by the dgrad-down epilogue),
+//                                  W13^T (backward cache [E, d, 2f])
 //   wgrad     dWd = dy^T h, dW13 = dgu^T x   all four quantised column-wise
 //             inside each expert's rows, stored group-transposed and padded
 //             to 128 rows, so the tokens are the contiguous K.
@@ -240,7 +241,8 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void mx_grouped_m_kernel(MxMParams mp)
 
     f32x16 acc[BM / 64][WL<NW>::NJ];
     mainloop_mx<BM, NW>(sa, sb, acc, smem);
-    epilogue_m<BM, EPI, NW>(acc, p, tile.row0, tile.rows_valid, nt, smem);
+    // the SwiGLU epilogues also write the row-wise MXFP8 h / dgu the next stage reads
+    epilogue_m<BM, EPI, NW, EPI != EPI_STORE>(acc, p, tile.row0, tile.rows_valid, nt, smem);
 }
 
 // weight gradient over group-transposed operands: C_e = A_e B_e^T with
@@ -407,10 +409,12 @@ size_t carve(void* ws, int E, int64_t R, int d, int f, MxWs* w)
 
 size_t gemm_ws_mxfp8(int E, int64_t n_rows, int d, int f) { return carve(nullptr, E, n_rows, d, f, nullptr) + 256; }
 
-// One stage of the MXFP8 grouped GEMM.  Each stage quantises the bf16
-// operands it reads (into the workspace) and then runs one block-scaled GEMM;
-// w13 / w2 are the forward caches for GATE_UP / DOWN and the backward
-// (transposed, column-quantised) caches for the two DGRAD stages.
+// One stage of the MXFP8 grouped GEMM: the quantisation of the bf16
+// operands it reads that no earlier stage left in the workspace, then one
+// block-scaled GEMM.  GATE_UP and DGRAD_DOWN also write the row-wise MXFP8
+// copy of their bf16 output (h, dgu) from their epilogues, which DOWN and
+// DGRAD_GATE_UP read.  w13 / w2 are the forward caches for GATE_UP / DOWN and
+// the backward (transposed, column-quantised) caches for the two DGRAD stages.
 hipError_t gemm_op_mxfp8(int op, const moe_gemm_tensors& t, GroupSpec g, int d, int f, void* ws,
                          hipStream_t s)
 {
@@ -435,13 +439,14 @@ hipError_t gemm_op_mxfp8(int op, const moe_gemm_tensors& t, GroupSpec g, int d, 
         a.p.ldc = 2 * f;
         a.p.H = static_cast<uint16_t*>(t.h);
         a.p.ldh = f;
+        a.p.Mq = w.hq;           // the row-wise MXFP8 h the down GEMM reads
+        a.p.Ms = w.hs;
+        a.p.ldq = f;
         a.Aq = static_cast<const uint8_t*>(t.x_perm);
         a.As = t.x_perm_scales;
         a.sBq = (int64_t)2 * f * d;
         return launch_mx_m<EPI_SWIGLU_FWD>(a, s);
-    case MOE_GEMM_DOWN:      // y = h Wd^T, h quantised along f
-        if ((err = launch_quantize_rows(static_cast<const uint16_t*>(t.h), R, f, w.hq, w.hs, s)) != hipSuccess)
-            return err;
+    case MOE_GEMM_DOWN:      // y = h Wd^T, h quantised along f (by the GATE_UP epilogue)
         a.p.N = d;
         a.p.K = f;
         a.p.ntn = (d + BN - 1) / BN;
@@ -462,15 +467,15 @@ hipError_t gemm_op_mxfp8(int op, const moe_gemm_tensors& t, GroupSpec g, int d, 
         a.p.ldc = 2 * f;
         a.p.G = static_cast<const uint16_t*>(t.gu);
         a.p.ldg = 2 * f;
+        a.p.Mq = w.dguq;         // the row-wise MXFP8 dgu the gate/up dgrad GEMM reads
+        a.p.Ms = w.dgus;
+        a.p.ldq = 2 * f;
         a.Aq = w.dyq;
         a.As = w.dys;
         a.sBq = (int64_t)f * d;
         return launch_mx_m<EPI_SWIGLU_BWD>(a, s);
-    case MOE_GEMM_DGRAD_GATE_UP:   // dx = [dg | du] [Wg ; Wu] (cache W13^T [E, d, 2f])
-        if ((err = launch_quantize_rows(static_cast<const uint16_t*>(t.dgu), R, 2 * f, w.dguq, w.dgus, s)) !=
-            hipSuccess)
-            return err;
-        a.p.N = d;
+    case MOE_GEMM_DGRAD_GATE_UP:   // dx = [dg | du] [Wg ; Wu] (cache W13^T [E, d, 2f]), dgu quantised along
+        a.p.N = d;                 // 2f by the DGRAD_DOWN epilogue
         a.p.K = 2 * f;
         a.p.ntn = (d + BN - 1) / BN;
         a.p.C = static_cast<uint16_t*>(t.dx_perm);

@@ -300,8 +300,7 @@ int moe_grouped_gemm_op(int op, int dtype, const moe_gemm_tensors* t,
         if ((w13_op && !t->w13_scales) || (w2_op && !t->w2_scales)) return MOE_EINVAL;
         if ((op == MOE_GEMM_GATE_UP || op == MOE_GEMM_WGRAD) && n_rows > 0 && !t->x_perm_scales)
             return MOE_EINVAL;
-        if (op != MOE_GEMM_GATE_UP &&
-            (!t->ws || t->ws_bytes < moe_gemm_workspace_bytes(dtype, E, n_rows, d, f) || !aligned16(t->ws)))
+        if (!t->ws || t->ws_bytes < moe_gemm_workspace_bytes(dtype, E, n_rows, d, f) || !aligned16(t->ws))
             return MOE_EWORKSPACE;
     }
     // operands each stage reads (r) and writes (w)

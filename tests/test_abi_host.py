@@ -146,13 +146,14 @@ def test_gemm_validation(m):
         assert lib.moe_grouped_gemm_bwd(m.MOE_BF16, P, P, None, P, P, P, None, P, None, P, 0, 8, 100,
                                         128, 128, P, P, P, P, ws, wsb, None) == m.MOE_EWORKSPACE
     # one MXFP8 stage: scales of the operands it reads, and the workspace for
-    # every stage but GATE_UP (which reads only the dispatch payload and weights)
+    # every stage (GATE_UP leaves the MXFP8 copy of h there for DOWN)
     t = m.MoeGemmTensors(**{n: P for n in m.GEMM_TENSOR_FIELDS})
     t.ws = None
 
     def op(o, t=t):
         return lib.moe_grouped_gemm_op(o, m.MOE_MXFP8, ctypes.byref(t), P, 0, 8, 100, 128, 128, None)
-    for o in (m.MOE_GEMM_DOWN, m.MOE_GEMM_DGRAD_DOWN, m.MOE_GEMM_DGRAD_GATE_UP, m.MOE_GEMM_WGRAD):
+    for o in (m.MOE_GEMM_GATE_UP, m.MOE_GEMM_DOWN, m.MOE_GEMM_DGRAD_DOWN, m.MOE_GEMM_DGRAD_GATE_UP,
+              m.MOE_GEMM_WGRAD):
         assert op(o) == m.MOE_EWORKSPACE
     t.ws, t.ws_bytes = P, lib.moe_gemm_workspace_bytes(m.MOE_MXFP8, 8, 100, 128, 128) - 1
     assert op(m.MOE_GEMM_DOWN) == m.MOE_EWORKSPACE
