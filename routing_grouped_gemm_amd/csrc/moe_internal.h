@@ -132,6 +132,21 @@ __device__ __forceinline__ int find_group(const int* s_pref, int E, int L)
 
 // ---------------------------------------------------------------- launch helpers
 constexpr int kRouteTokensPerBlock = 64;
+// The route's finalize handles S histogram blocks of 64 tokens per
+// workgroup: S = 1 below 65536 tokens, else as many as keep its pairs within
+// kRouteMaxPairsPerBlock (at most 16), so that large batches write their
+// source slots in fewer, longer per-expert runs of destination rows.
+constexpr int kRouteMaxPairsPerBlock = 4096;
+constexpr int kRouteMaxChunkCounts = 8192;   // (pairs / 64) x experts of one finalize workgroup
+inline int route_subblocks(int64_t T, int E, int k)
+{
+    if (T < 65536) return 1;
+    int s = kRouteMaxPairsPerBlock / (kRouteTokensPerBlock * k);
+    const int s2 = kRouteMaxChunkCounts / (k * E);
+    s = s < s2 ? s : s2;
+    return s < 16 ? (s < 1 ? 1 : s) : 16;
+}
+
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 8;
 constexpr int kMxColPad = 128;   // column-wise MXFP8 groups are padded to this many rows

@@ -72,21 +72,20 @@ __global__ __launch_bounds__(NTHR) void route_topk_kernel(const float* __restric
                                                          int32_t* __restrict__ dev_err)
 {
     constexpr int TPI = NTHR / LPT;  // tokens handled concurrently by the block
-    static_assert(VPL <= 32, "taken mask");
-    __shared__ int s_exp[TB * kMaxTopK];
     __shared__ int s_hist[kMaxExperts];
 
     const int tid = threadIdx.x;
     const int lane = tid % LPT;
     const int seg = tid / LPT;
-    const int t0 = blockIdx.x * TB;
-    const int nt = min(TB, T - t0);
     // 16-byte loads of whole lane ranges when every row start is 16-byte aligned
     const bool vec = (E % 4) == 0 && (VPL % 4) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
 
     for (int e = tid; e < E; e += NTHR) s_hist[e] = 0;
+    __syncthreads();
 
     bool bad = false;
+    const int t0 = blockIdx.x * TB;
+    const int nt = min(TB, T - t0);
     for (int tl = seg; tl < TB; tl += TPI) {
         const int t = t0 + tl;
         const bool active = tl < nt;
@@ -160,42 +159,51 @@ __global__ __launch_bounds__(NTHR) void route_topk_kernel(const float* __restric
                 if (j < k) {
                     topk_idx[(int64_t)t * k + j] = sel_i[j];
                     topk_w[(int64_t)t * k + j] = ex[j] / den;
-                    s_exp[tl * k + j] = sel_i[j];
+                    atomicAdd(&s_hist[sel_i[j]], 1);   // integer count: order-independent
                 }
             }
         }
     }
     if (bad && dev_err) atomicOr(dev_err, (int)MOE_ERR_NONFINITE_LOGIT);
     __syncthreads();
-
-    // the block's pairs per expert
-    const int P = nt * k;
-    for (int p = tid; p < P; p += NTHR) atomicAdd(&s_hist[s_exp[p]], 1);  // integer count: order-independent
-    __syncthreads();
     // expert-major: hist[e][block]
     for (int e = tid; e < E; e += NTHR) hist[(int64_t)e * nblk + blockIdx.x] = s_hist[e];
 }
 
-// One workgroup of 256 threads per expert: hist [E, nblk] (expert-major) is
+// One workgroup of SNT threads per expert: hist [E, nblk] (expert-major) is
 // replaced by its exclusive prefix along each expert's row (the first rank
 // of each block per expert) and counts[e] is the row total.  Per chunk of
-// 256 * SCH blocks each thread sums SCH consecutive entries (all loads in
-// flight together), the wave sums are scanned through LDS, and the chunk's
-// total carries into the next.
-constexpr int SCH = 16;
-__global__ __launch_bounds__(256) void route_scan_kernel(int32_t* __restrict__ hist, int nblk,
+// SNT * SCH blocks (all of a 2^20-token batch's 16384 in one pass) each
+// thread sums SCH consecutive entries (all loads in flight together), the
+// wave sums are scanned through LDS, and the chunk's total carries into the
+// next.
+constexpr int SCH = 16, SNT = 1024;
+__global__ __launch_bounds__(SNT) void route_scan_kernel(int32_t* __restrict__ hist, int nblk,
                                                          int E, int32_t* __restrict__ counts)
 {
-    __shared__ int s_w[4];
+    constexpr int NWS = SNT / 64;
+    __shared__ int s_w[NWS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int e = blockIdx.x;
     int32_t* row = hist + (int64_t)e * nblk;
+    const bool vec = (nblk & 3) == 0 && (reinterpret_cast<uintptr_t>(hist) & 15) == 0;
     int carry = 0;
-    for (int c0 = 0; c0 < nblk; c0 += 256 * SCH) {
+    for (int c0 = 0; c0 < nblk; c0 += SNT * SCH) {
         const int b0 = c0 + tid * SCH;
         int v[SCH];
+        if (vec && b0 + SCH <= nblk) {       // whole 16-byte vectors
 #pragma unroll
-        for (int q = 0; q < SCH; ++q) v[q] = b0 + q < nblk ? row[b0 + q] : 0;
+            for (int q = 0; q < SCH / 4; ++q) {
+                const int4 w = reinterpret_cast<const int4*>(row + b0)[q];
+                v[4 * q] = w.x;
+                v[4 * q + 1] = w.y;
+                v[4 * q + 2] = w.z;
+                v[4 * q + 3] = w.w;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < SCH; ++q) v[q] = b0 + q < nblk ? row[b0 + q] : 0;
+        }
         int sum = 0;
 #pragma unroll
         for (int q = 0; q < SCH; ++q) sum += v[q];
@@ -209,15 +217,31 @@ __global__ __launch_bounds__(256) void route_scan_kernel(int32_t* __restrict__ h
         __syncthreads();
         int before = carry, chunk = 0;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < NWS; ++w) {
             if (w < wave) before += s_w[w];
             chunk += s_w[w];
         }
         int run = before + incl - sum;
+        if (vec && b0 + SCH <= nblk) {
 #pragma unroll
-        for (int q = 0; q < SCH; ++q) {
-            if (b0 + q < nblk) row[b0 + q] = run;
-            run += v[q];
+            for (int q = 0; q < SCH / 4; ++q) {
+                int4 w;
+                w.x = run;
+                run += v[4 * q];
+                w.y = run;
+                run += v[4 * q + 1];
+                w.z = run;
+                run += v[4 * q + 2];
+                w.w = run;
+                run += v[4 * q + 3];
+                reinterpret_cast<int4*>(row + b0)[q] = w;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < SCH; ++q) {
+                if (b0 + q < nblk) row[b0 + q] = run;
+                run += v[q];
+            }
         }
         carry += chunk;
         __syncthreads();   // s_w is rewritten by the next chunk
@@ -259,58 +283,117 @@ __device__ __forceinline__ void block_offsets(const int32_t* __restrict__ counts
     __syncthreads();
 }
 
-// One workgroup per block of TB tokens (FT threads: a wave per 64 pairs, all
-// of a block's TB * k <= 512 pairs at once).  The expert offsets come first
-// (exclusive scan of counts; block 0 stores them).  A pair's rank among its
-// block's earlier pairs of the same expert: lane l of wave w holds pair
-// 64 w + l; one ballot per bit of the expert index gives the mask of the
-// wave's lanes with the same expert, its population below l is the rank in
-// the wave, and the wave's per-expert counts (written by the first lane of
-// each expert) add the earlier waves' pairs.  Then
-// dst_row = offsets[e] + base[e][block] + rank (or e * C + rank when below
-// the capacity C, else -1) and src_slot[dst] = pair.  With C > 0 every row
-// of [e * C + counts[e], (e + 1) * C) gets src_slot -1 (grid-stride).
+// One workgroup per route block: S consecutive histogram blocks of TB tokens,
+// whose pairs are a contiguous run of the pair index, taken as chunks of 64
+// (FT threads; wave w takes chunks w, w + 8, ...).
+//  - Every chunk's expert indices are loaded first (one memory round trip).
+//  - A pair's rank among the route block's earlier pairs of the same expert:
+//    per chunk, one wave ballot per bit of the expert index gives each lane
+//    the mask of the chunk's lanes with its expert (its population below the
+//    lane is the rank in the chunk, its first lane records the chunk's count
+//    of that expert); one thread per expert then turns the per-chunk counts
+//    into prefixes over the chunks, whose total is the block's count of the
+//    expert, and X is the exclusive scan of those totals over the experts.
+//  - dst_row = offsets[e] + base[e][block] + rank (or e * C + rank when below
+//    the capacity C, else -1) goes out per pair (offsets = exclusive scan of
+//    counts, block 0 stores them); the pair is also placed at X[e] + rank in
+//    LDS, so that src_slot leaves as one run of consecutive rows per expert
+//    instead of a scatter.
+//  - With C > 0 every row of [e * C + counts[e], (e + 1) * C) gets src_slot
+//    -1 (grid-stride).
 constexpr int FT = TB * kMaxTopK;   // 512 threads
 __global__ __launch_bounds__(FT) void route_finalize_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ base, int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ counts, int T, int E, int k, int C, int nblk, int nbits,
+    const int32_t* __restrict__ counts, int T, int E, int k, int C, int nsub, int S, int nbits,
     int32_t* __restrict__ dst_row, int32_t* __restrict__ src_slot)
 {
     constexpr int NWF = FT / 64;
+    constexpr int CPW = kRouteMaxPairsPerBlock / FT;     // chunks per wave, at most
     __shared__ int s_off[kMaxExperts + 1];
+    __shared__ int s_x[kMaxExperts + 1];
     __shared__ int s_wsum[NWF];
-    __shared__ int s_cnt[NWF][kMaxExperts];
+    __shared__ int s_tot[kMaxExperts];
+    __shared__ int s_cnt[kRouteMaxChunkCounts];          // [chunk][expert]
+    __shared__ int s_pair[kRouteMaxPairsPerBlock];
+    __shared__ uint16_t s_e[kRouteMaxPairsPerBlock];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int q = tid; q < NWF * kMaxExperts; q += FT) (&s_cnt[0][0])[q] = 0;
-    block_offsets<FT>(counts, E, s_off, s_wsum);   // (its barriers also order the clearing above)
-    if (blockIdx.x == 0)
-        for (int e = tid; e <= E; e += FT) offsets[e] = s_off[e];
     const int b = blockIdx.x;
-    const int t0 = b * TB;
-    const int P = b < nblk ? min(TB, T - t0) * k : 0;
-    const int p = tid;                                   // this thread's pair of the block
-    const bool valid = p < P;
-    const int64_t i = (int64_t)t0 * k + p;
-    const int e = valid ? topk_idx[i] : 0;
-    // lanes of this wave with the same expert
-    uint64_t same = __ballot(valid);
-    for (int bit = 0; bit < nbits; ++bit) {
-        const uint64_t on = __ballot(valid && ((e >> bit) & 1));
-        same &= ((e >> bit) & 1) ? on : ~on;
+    const int sb0 = b * S;                               // first histogram block
+    const int64_t p0 = (int64_t)sb0 * TB * k;            // first pair
+    const int64_t PB64 = sb0 < nsub ? min((int64_t)S * TB, (int64_t)T - (int64_t)sb0 * TB) * k : 0;
+    const int PB = (int)(PB64 > 0 ? PB64 : 0);           // pairs of this route block
+    const int nch = (PB + 63) / 64;
+    int ev[CPW];
+#pragma unroll
+    for (int q = 0; q < CPW; ++q) {
+        const int p = (wave + q * NWF) * 64 + lane;
+        ev[q] = p < PB ? topk_idx[p0 + p] : 0;
     }
+    for (int q = tid; q < nch * E; q += FT) s_cnt[q] = 0;
+    block_offsets<FT>(counts, E, s_off, s_wsum);         // (its barriers also order the clearing above)
+    if (b == 0)
+        for (int e = tid; e <= E; e += FT) offsets[e] = s_off[e];
+    // per chunk: rank in the chunk, chunk count per expert
+    int rk[CPW];
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int rank = __popcll(same & below);
-    // per-wave counts of the experts this wave holds (the first lane of each writes)
-    if (valid && rank == 0) s_cnt[wave][e] = __popcll(same);
+#pragma unroll
+    for (int q = 0; q < CPW; ++q) {
+        const int c = wave + q * NWF;
+        const bool valid = c * 64 + lane < PB;
+        const int e = ev[q];
+        uint64_t same = __ballot(valid);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const uint64_t on = __ballot(valid && ((e >> bit) & 1));
+            same &= ((e >> bit) & 1) ? on : ~on;
+        }
+        rk[q] = __popcll(same & below);
+        if (valid && rk[q] == 0) s_cnt[c * E + e] = __popcll(same);
+    }
     __syncthreads();
-    if (valid) {
-        for (int w = 0; w < wave; ++w) rank += s_cnt[w][e];
-        rank += base[(int64_t)e * nblk + b];
+    // per expert: prefixes over the chunks and the block's total
+    for (int e = tid; e < E; e += FT) {
+        int run = 0;
+        for (int c = 0; c < nch; ++c) {
+            const int v = s_cnt[c * E + e];
+            s_cnt[c * E + e] = run;
+            run += v;
+        }
+        s_tot[e] = run;
+    }
+    __syncthreads();
+    // one histogram block (small batches): runs of a pair or two per expert,
+    // src_slot is written straight from each pair
+    const bool staged = S > 1;
+    if (staged) block_offsets<FT>(s_tot, E, s_x, s_wsum);   // LDS source; its barriers order the reads
+#pragma unroll
+    for (int q = 0; q < CPW; ++q) {
+        const int c = wave + q * NWF;
+        const int p = c * 64 + lane;
+        if (p < PB) {
+            const int e = ev[q];
+            const int loc = s_cnt[c * E + e] + rk[q];
+            const int rank = base[(int64_t)e * nsub + sb0] + loc;
+            int64_t dst;
+            if (C > 0) dst = rank < C ? (int64_t)e * C + rank : -1;
+            else dst = (int64_t)s_off[e] + rank;
+            dst_row[p0 + p] = (int32_t)dst;
+            if (staged) {
+                s_pair[s_x[e] + loc] = (int32_t)(p0 + p);
+                s_e[s_x[e] + loc] = (uint16_t)e;
+            } else if (dst >= 0) {
+                src_slot[dst] = (int32_t)(p0 + p);
+            }
+        }
+    }
+    if (staged) __syncthreads();
+    // src_slot, one run of consecutive rows per expert
+    for (int q = tid; staged && q < PB; q += FT) {
+        const int e = s_e[q];
+        const int rank = base[(int64_t)e * nsub + sb0] + (q - s_x[e]);
         int64_t dst;
         if (C > 0) dst = rank < C ? (int64_t)e * C + rank : -1;
         else dst = (int64_t)s_off[e] + rank;
-        dst_row[i] = (int32_t)dst;
-        if (dst >= 0) src_slot[dst] = (int32_t)i;
+        if (dst >= 0) src_slot[dst] = s_pair[q];
     }
     if (C > 0) {
         const int64_t rows = (int64_t)E * C;
@@ -398,7 +481,8 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int capacity, 
                         int32_t* src_slot, int64_t n_rows, int32_t* hist, int32_t* dev_err, hipStream_t s)
 {
     (void)n_rows;
-    const int nblk = (T + TB - 1) / TB;
+    const int S = route_subblocks(T, E, k);    // histogram blocks per finalize workgroup
+    const int nblk = (T + TB - 1) / TB;          // histogram blocks (top-k workgroups)
     if (nblk > 0) {
         // 16 logits per lane (8 below 9 experts): a token's segment is E/16 lanes
         if (E <= 8) launch_topk<1, 8>(nblk, s, logits, T, E, k, topk_idx, topk_w, hist, dev_err);
@@ -411,14 +495,15 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int capacity, 
         else launch_topk<64, 16>(nblk, s, logits, T, E, k, topk_idx, topk_w, hist, dev_err);
     }
     // also for T = 0: the scan then writes zero counts
-    hipLaunchKernelGGL(route_scan_kernel, dim3((unsigned)E), dim3(256), 0, s, hist, nblk, E, counts);
+    hipLaunchKernelGGL(route_scan_kernel, dim3((unsigned)E), dim3(SNT), 0, s, hist, nblk, E, counts);
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     // at least one block: it stores the offsets; padded rows beyond the counts
     // are covered grid-stride by however many blocks there are
-    const int grid = nblk > 0 ? nblk : 1;
+    const int nroute = (nblk + S - 1) / S;
+    const int grid = nroute > 0 ? nroute : 1;
     hipLaunchKernelGGL(route_finalize_kernel, dim3((unsigned)grid), dim3(FT), 0, s, topk_idx, hist, offsets,
-                       counts, T, E, k, capacity, nblk, nbits, dst_row, src_slot);
+                       counts, T, E, k, capacity, nblk, S, nbits, dst_row, src_slot);
     return hipGetLastError();
 }
 
