@@ -83,6 +83,23 @@ def test_route_padded(moe, T, E, k, C):
     _check_route(lay, oracle.route(logits.numpy(), k, capacity=C))
 
 
+# Batches of 65536 tokens and more: the finalize takes up to 16 histogram
+# blocks per workgroup and writes source slots as per-expert runs (a ragged
+# last block, padded layouts with drops, k = 8, and ties)
+@pytest.mark.parametrize("T,E,k,C,routing", [(262144, 128, 4, 0, "uniform"), (200003, 64, 2, 7000, "zipf"),
+                                             (70001, 16, 8, 0, "uniform"), (65536, 1024, 3, 0, "ties")])
+def test_route_large_batch_bit_exact(moe, T, E, k, C, routing):
+    _say("route-large", T, E, k, C, routing)
+    if routing == "ties":
+        g = torch.Generator().manual_seed(T)
+        logits = torch.randint(-3, 4, (T, E), generator=g).float()
+    else:
+        logits = moe_synth.router_logits(T, E, seed=T + E, routing=routing)
+    lay = _gpu_route(moe, logits, k, capacity=C)
+    _check_route(lay, oracle.route(logits.numpy(), k, capacity=C))
+    assert int(lay.dev_err.item()) == 0
+
+
 def test_route_empty_and_nonfinite(moe):
     _say("route-empty")
     lay = _gpu_route(moe, torch.zeros(0, 8), 2)
