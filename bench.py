@@ -37,7 +37,7 @@ KERNEL_NAMES = {
     "gemm_down": "gemm_grouped_m_kernel<256, 64, 2, false, 0, 8, true> (down)",
     "gemm_dgrad_down": "gemm_grouped_m_kernel<256, 64, 2, true, 2, 8, true> (dgrad down + SwiGLU bwd)",
     "gemm_dgrad_gate_up": "gemm_grouped_m_kernel<256, 64, 2, true, 0, 8, true> (dgrad gate/up)",
-    "gemm_wgrad": "gemm_grouped_k_kernel<256, 64, 2, 8> (wgrad, dWd and dW13 in one launch)",
+    "gemm_wgrad": "k_deal_flag_kernel + gemm_grouped_k_persistent<8> (wgrad, dWd and dW13 in one launch)",
     "permute": "permute_kernel<true, false, {k}>",
     "combine": "combine_kernel<true, {k}>",
     "combine_bwd": "permute_kernel<true, true, {k}>",
@@ -46,10 +46,10 @@ KERNEL_NAMES = {
 }
 KERNEL_NAMES_MX = {
     "gemm_gate_up": "mx_grouped_m_kernel<256, 1, 8> (gate/up + SwiGLU)",
-    "gemm_down": "quant_rows_kernel (h) + mx_grouped_m_kernel<256, 0, 8> (down)",
+    "gemm_down": "mx_grouped_m_kernel<256, 0, 8> (down; h quantised by the gate/up epilogue)",
     "gemm_dgrad_down": "quant_rows_kernel (dy) + mx_grouped_m_kernel<256, 2, 8> (dgrad down + SwiGLU bwd)",
-    "gemm_dgrad_gate_up": "quant_rows_kernel (dgu) + mx_grouped_m_kernel<256, 0, 8> (dgrad gate/up)",
-    "gemm_wgrad": "4 x quant_cols_kernel + mx_grouped_k_kernel<256, 8> (wgrad, dWd and dW13)",
+    "gemm_dgrad_gate_up": "mx_grouped_m_kernel<256, 0, 8> (dgrad gate/up; dgu quantised by the dgrad-down epilogue)",
+    "gemm_wgrad": "4 x quant_cols_kernel + mx_k_deal_flag_kernel + mx_grouped_k_kernel<256, 8> (wgrad, dWd and dW13)",
     "permute": "permute_mx_kernel",
     "combine": "combine_kernel<true, {k}>",
     "combine_bwd": "permute_kernel<true, true, {k}>",
