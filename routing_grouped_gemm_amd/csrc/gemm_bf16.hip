@@ -45,8 +45,12 @@ using namespace gemm;
 // launch.  Runs of 16 measured the same, 32 slower.
 constexpr int kKDealRun = 4;
 // The direct loads of the next K-step go out spread evenly over the first
-// kLoadSpan / 32 of a K-step's MFMAs (single-group loop; best of 8 .. 28).
+// kLoadSpan / 32 of a K-step's MFMAs (single-group loop, two LDS stages;
+// best of 8 .. 28).  With a deeper ring the loads of K-step kt + NS - 1 go
+// out over the first kLoadSpanRing / 32 of K-step kt's MFMAs.
 constexpr int kLoadSpan = 12;
+constexpr int kLoadSpanRing = 32;
+
 
 // One MFMA operand fragment (8 consecutive k of one row) for lane `lane`:
 // tile row row_base + (lane & 31), k = ks*16 + (lane >> 5)*8 + [0, 8).
@@ -83,18 +87,25 @@ __device__ __forceinline__ bf16x8 read_frag(const uint16_t* tile, int row_base, 
     }
 }
 
-// BM x 256 tile over s.K, accumulators acc[BM/64][NJ].  Two LDS stages of
-// (BM + 256) x BK bf16: the direct loads of K-step kt+1 are in flight while
-// the MFMAs of K-step kt run; one barrier per K-step.  Fragments of k-slice
-// ks+1 are read while the MFMAs of slice ks run, and the MFMAs of each
-// K-step's last slice are issued after the next barrier, so that they cover
-// the latency of the first fragment reads of the new K-step.
-// PRE: K-step 0 was already issued into stage 0 by the caller (with loaders
-// made from the same sources); STORES16: the caller issued exactly 16 vector
-// memory operations per wave after those loads (and nothing else since), so
-// K-step 0 has landed once at most 16 are outstanding (vector memory
-// operations complete in issue order) and those may drain during K-step 0.
-template <int BM, int BK, int NS, bool A_MN, bool B_MN, int NW, bool KAL, bool PRE = false>
+// BM x 256 tile over s.K, accumulators acc[BM/64][NJ].  A ring of NS LDS
+// stages of (BM + 256) x BK bf16: the direct loads of K-step kt + NS - 1 are
+// in flight while the MFMAs of K-step kt run; one barrier per K-step.  With
+// more than two stages (both operands MN-major, or K a multiple of BK) every
+// K-step issues the loads NS - 1 steps ahead, past the end of K too, where
+// they take an offset outside the buffer and write zeros to a stage nobody
+// reads (a tail loop without loads made the accumulators spill).  The wait
+// at a K-step counts the vector memory operations issued after its loads:
+// they complete in issue order, those with every lane outside the buffer
+// included (checked on the hardware for direct-to-LDS loads and for stores).
+// Fragments of k-slice ks+1 are read while the MFMAs of slice ks run, and the
+// MFMAs of each K-step's last slice are issued after the next barrier, so
+// that they cover the latency of the first fragment reads of the new K-step.
+// PRE: K-steps 0 .. PRE-1 were already issued into stages 0 .. PRE-1 by the
+// caller (with loaders made from the same sources); stores16: the caller
+// issued exactly 16 vector memory operations per wave after those loads (and
+// nothing else since), so they are waited for only from K-step PRE on and
+// may drain during the first K-steps.
+template <int BM, int BK, int NS, bool A_MN, bool B_MN, int NW, bool KAL, int PRE = 0>
 __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
                                          f32x16 (&acc)[BM / 64][WL<NW>::NJ], uint16_t* smem,
                                          bool stores16 = false)
@@ -109,8 +120,11 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
     constexpr int NB = LB::PER_WAVE;
     constexpr int NQ = NA + NB;                    // load instructions per wave per K-step
     constexpr int SM = MI * NJ;                    // MFMAs per k-slice
-    constexpr int SPAN = kLoadSpan * KS * SM / 32 < NQ ? NQ : kLoadSpan * KS * SM / 32;
-    static_assert(NS == 2, "two LDS stages");
+    constexpr int SPN = (NS == 2 ? kLoadSpan : kLoadSpanRing) * KS * SM / 32;
+    constexpr int SPAN = SPN < NQ ? NQ : SPN;
+    static_assert(NS >= 2 && (NS & (NS - 1)) == 0, "a power-of-two ring of LDS stages");
+    static_assert(NS == 2 || KAL || (A_MN && B_MN), "deeper rings issue loads without the K-tail test");
+    static_assert(PRE >= 0 && PRE < NS, "pre-issued K-steps fit the ring");
     static_assert(KS >= 2 && KS % 2 == 0, "an even number of k-slices per K-step");
     static_assert(SPAN <= KS * SM, "the loads fit the K-step's MFMAs");
     const int tid = threadIdx.x;
@@ -132,9 +146,17 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
     LB lb;
     la.init(sa, lds_addr(smem));
     lb.init(sb, lds_addr(smem + BM * BK));
-    if constexpr (!PRE) {
-        la.issue(smem, 0);
-        lb.issue(smem + BM * BK, 0);
+#pragma unroll
+    for (int j = PRE; j <= NS - 2; ++j) {
+        if constexpr (NS == 2) {
+            la.issue(smem + j * STAGE, j);
+            lb.issue(smem + j * STAGE + BM * BK, j);
+        } else {
+#pragma unroll
+            for (int q = 0; q < NA; ++q) la.issue_ring((uint32_t)(j * STAGE * 2), j, q, j < nk);
+#pragma unroll
+            for (int q = 0; q < NB; ++q) lb.issue_ring((uint32_t)(j * STAGE * 2), j, q, j < nk);
+        }
     }
 
     bf16x8 af[2][MI], bfr[2][NJ];
@@ -195,17 +217,26 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
     // 2: loads with the K-tail test, if there is a next K-step; 0: no loads
     auto kstep = [&](int kt, auto MODE) __attribute__((always_inline)) {
         constexpr int md = decltype(MODE)::value;
-        // this wave's loads of K-step kt have landed
-        if (PRE && kt == 0 && stores16) wait_vmcnt<16>();
-        else wait_vmcnt<0>();
-        __syncthreads();     // everyone's have, and the other stage is no longer read
-        const uint16_t* a_s = smem + (kt & 1) * STAGE;
+        // this wave's loads of K-step kt have landed (those of the NS - 2
+        // K-steps after it, and stores the caller issued after them, may not)
+        if (PRE > 0 && stores16 && kt < PRE) wait_vmcnt<NQ * (NS - 2) + 16>();
+        else wait_vmcnt<NQ * (NS - 2)>();
+        __syncthreads();     // everyone's have, and the stage loaded next is no longer read
+        int so = (kt & (NS - 1)) * STAGE;
+        // one stage base in a scalar register, rather than per-stage copies
+        // of every fragment address kept live across the loop
+        if constexpr (NS > 2) asm volatile("" : "+s"(so));
+        const uint16_t* a_s = smem + so;
         const uint16_t* b_s = a_s + BM * BK;
-        const uint32_t nso = (uint32_t)(((kt + 1) & 1) * STAGE * 2);   // next stage, bytes
+        const int kn = kt + NS - 1;                                      // the K-step loaded now
+        const uint32_t nso = (uint32_t)((kn & (NS - 1)) * STAGE * 2);    // its stage, bytes
         auto load = [&](int q) __attribute__((always_inline)) {
-            if constexpr (md == 1) {
-                if (q < NA) la.issue_fast(nso, kt + 1, q);
-                else lb.issue_fast(nso, kt + 1, q - NA);
+            if constexpr (md == 1 && NS > 2) {
+                if (q < NA) la.issue_ring(nso, kn, q, kn < nk);
+                else lb.issue_ring(nso, kn, q - NA, kn < nk);
+            } else if constexpr (md == 1) {
+                if (q < NA) la.issue_fast(nso, kn, q);
+                else lb.issue_fast(nso, kn, q - NA);
             } else if (md == 2 && kt + 1 < nk) {
                 uint16_t* nxt = smem + ((kt + 1) & 1) * STAGE;
                 if (q < NA) la.issue_one(nxt, kt + 1, q);
@@ -239,14 +270,17 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
         }
     };
     // KAL: K is a multiple of BK (or both operands are MN-major), so every
-    // next K-step lies inside K
-    if constexpr (KAL || (A_MN && B_MN)) {
+    // K-step loaded lies inside K
+    if constexpr (NS == 2 && (KAL || (A_MN && B_MN))) {
         for (int kt = 0; kt + 1 < nk; ++kt) kstep(kt, std::integral_constant<int, 1>{});
         kstep(nk - 1, std::integral_constant<int, 0>{});
+    } else if constexpr (NS > 2) {
+        for (int kt = 0; kt < nk; ++kt) kstep(kt, std::integral_constant<int, 1>{});
     } else {
         for (int kt = 0; kt < nk; ++kt) kstep(kt, std::integral_constant<int, 2>{});
     }
     slice(1, KS * SM, [](int) __attribute__((always_inline)) {});   // the last k-slice of the last K-step
+    if constexpr (NS > 2) wait_vmcnt<0>();   // the zero loads past K have landed too
     __syncthreads();  // the LDS may be reused by the caller
 }
 
@@ -778,24 +812,33 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_kernel(KParams p)
 // the tiles of its XCD's list (the contiguous range or the dealt runs the
 // flag kernel chose), taking positions from that XCD's counter in the
 // workspace, so tiles of very different K (their group's rows) still spread
-// evenly over the CUs.  Per tile, the same main loop and arithmetic as
-// gemm_grouped_k_kernel; between two tiles:
-//   - the next position is fetched while the current tile computes;
-//   - the next tile's first K-step goes out to LDS stage 0 before the current
-//     tile's epilogue, whose latency then hides under the epilogue;
-//   - the epilogue stages the result in stage 1, 128 rows at a time, and
-//     leaves through 16 buffer stores per wave that are always issued (out of
-//     range elements are dropped by the buffer's range), so the next tile's
-//     first wait is "at most 16 outstanding" and the stores drain while its
-//     first K-step computes, instead of every CU storing at once while none
-//     computes.
+// evenly over the CUs.  Per tile, the arithmetic of gemm_grouped_k_kernel
+// (the same MFMAs in the same k order), with K-steps of 32 through a ring of
+// four LDS stages, so that the loads of a K-step go out three K-steps ahead
+// of its MFMAs (two stages of 64 left the loads of the next K-step too little
+// time under load).  Between two tiles:
+//   - the next position is fetched while the current tile computes, and the
+//     group bounds come from a copy in LDS made at the start;
+//   - the next tile's first two K-steps go out to stages 0 and 1 before the
+//     current tile's epilogue, whose latency then hides under the epilogue;
+//   - the epilogue stages the result in stages 2 and 3, 128 rows at a time,
+//     and leaves through 16 buffer stores per wave that are always issued
+//     (out of range elements are dropped by the buffer's range), so the next
+//     tile waits for the stores only from its third K-step on and they drain
+//     while its first K-steps compute, instead of every CU storing at once
+//     while none computes.  (Storing from the accumulators without LDS, 32
+//     bytes of each of 32 rows per instruction, measured 3.1 ms against
+//     2.8 ms at e128 with plain stores and 6.6 ms non-temporal.)
 template <int NW>
 __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_persistent(KParams p)
 {
-    constexpr int BM = 256, BK = 64, NS = 2;
+    constexpr int BM = 256, BK = 32, NS = 4, PRE = 2;
     constexpr int STAGE = (BM + BN) * BK;           // elements per stage
+    static_assert(2 * STAGE * 2 == 128 * BN * 2, "stages 2 and 3 hold 128 staged output rows");
     __shared__ __align__(16) uint16_t smem[NS * STAGE];
     __shared__ int s_pos[2];
+    __shared__ int64_t s_gb[kMaxExperts + 1];       // group bounds
+    for (int g = threadIdx.x; g <= p.E; g += blockDim.x) s_gb[g] = group_begin(p.group_off, p.capacity, g, p.n_rows);
     const int t0 = p.pr[0].mtn * p.pr[0].ntn;
     const int tiles_e = t0 + (p.nprob > 1 ? p.pr[1].mtn * p.pr[1].ntn : 0);
     const int total = p.E * tiles_e;
@@ -829,8 +872,8 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_persistent(KParams p
                      t.mt, t.nt);
         t.mt = __builtin_amdgcn_readfirstlane(t.mt);
         t.nt = __builtin_amdgcn_readfirstlane(t.nt);
-        const int64_t g0 = group_begin(p.group_off, p.capacity, t.e, p.n_rows);
-        const int64_t g1 = group_begin(p.group_off, p.capacity, t.e + 1, p.n_rows);
+        const int64_t g0 = s_gb[t.e];
+        const int64_t g1 = s_gb[t.e + 1];
         t.g0 = uni64(g0);
         t.m_e = __builtin_amdgcn_readfirstlane((int)max((int64_t)0, g1 - g0));
     };
@@ -847,7 +890,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_persistent(KParams p
         sb.rows1 = 0;
         sb.K = t.m_e;
     };
-    // K-step 0 of tile t into stage 0 (nothing for an empty group)
+    // K-steps 0 .. PRE-1 of tile t into stages 0 .. PRE-1
     auto first_loads = [&](const KT& t) __attribute__((always_inline)) {
         if (t.m_e == 0) return;
         TileSrc sa, sb;
@@ -858,8 +901,17 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_persistent(KParams p
         asm volatile("" : "+v"(tid));    // recomputed here, not kept live across the tile loop
         la.init_tid(sa, lds_addr(smem), tid);
         lb.init_tid(sb, lds_addr(smem + BM * BK), tid);
-        la.issue(smem, 0);
-        lb.issue(smem + BM * BK, 0);
+        // (LDS byte addresses through M0, no generic pointers kept live;
+        // K-steps past the group's rows load zeros)
+#pragma unroll
+        for (int j = 0; j < PRE; ++j) {
+#pragma unroll
+            for (int i = 0; i < decltype(la)::PER_WAVE; ++i)
+                la.issue_ring((uint32_t)(j * STAGE * 2), j, i, j * BK < t.m_e);
+#pragma unroll
+            for (int i = 0; i < decltype(lb)::PER_WAVE; ++i)
+                lb.issue_ring((uint32_t)(j * STAGE * 2), j, i, j * BK < t.m_e);
+        }
     };
 
     if (threadIdx.x == 0) s_pos[1] = atomicAdd(counter, 1);
@@ -876,7 +928,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_persistent(KParams p
         TileSrc sa, sb;
         sources(cur, sa, sb);
         f32x16 acc[BM / 64][WL<NW>::NJ];
-        mainloop<BM, BK, NS, true, true, NW, true, true>(sa, sb, acc, smem, stores16);
+        mainloop<BM, BK, NS, true, true, NW, true, PRE>(sa, sb, acc, smem, stores16);
         if (threadIdx.x == 0) s_pos[it & 1] = pos;
         __syncthreads();
         const int Ln = tile_at(s_pos[it & 1]);
@@ -888,9 +940,9 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_persistent(KParams p
         const KProblem& q = cur.which ? p.pr[1] : p.pr[0];
         uint16_t* Ct = q.C + (int64_t)cur.e * q.sC + (int64_t)cur.mt * BM * q.ldc;
         const int rows = q.M - cur.mt * BM;
-        uint8_t* stage1 = reinterpret_cast<uint8_t*>(smem + STAGE);
-        store_half_nt<NW>(acc, Ct, q.ldc, rows, cur.nt * BN, q.N, stage1, 0);
-        store_half_nt<NW>(acc, Ct, q.ldc, rows, cur.nt * BN, q.N, stage1, 1);
+        uint8_t* stage23 = reinterpret_cast<uint8_t*>(smem + 2 * STAGE);
+        store_half_nt<NW>(acc, Ct, q.ldc, rows, cur.nt * BN, q.N, stage23, 0);
+        store_half_nt<NW>(acc, Ct, q.ldc, rows, cur.nt * BN, q.N, stage23, 1);
         if (Ln >= total) return;
         cur = nxt;
         stores16 = true;

@@ -193,6 +193,16 @@ struct DirectLoader {
         dma16_to_lds_at(hi ? r1 : r0, m0w + stage_off + (uint32_t)(i * NW * 1024), off[i],
                         (uint32_t)kt * kstep);
     }
+    // issue_fast, or (inside false) the same instruction with the scalar
+    // offset at the buffer's range, so that every lane's offset lies past it
+    // (and below 2^32 for the masked lanes at kOOB): it writes zeros to its
+    // LDS chunk without a memory access
+    __device__ __forceinline__ void issue_ring(uint32_t stage_off, int kt, int i, bool inside)
+    {
+        const bool hi = half_of(i);
+        const desc_t d = hi ? r1 : r0;
+        dma16_to_lds_at(d, m0w + stage_off + (uint32_t)(i * NW * 1024), off[i], inside ? (uint32_t)kt * kstep : d[2]);
+    }
     // global -> LDS for K-step kt into the tile at `tile` (TILE_BYTES bytes)
     __device__ __forceinline__ void issue(uint16_t* tile, int kt)
     {

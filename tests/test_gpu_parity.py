@@ -188,6 +188,36 @@ def test_layer_fwd_bwd_parity(moe, T, d, E, f, k, dtype, C):
         assert torch.all(lay.dw13[E - 2] == 0) and torch.all(lay.dw2[E - 2] == 0)
 
 
+def test_layer_group_sizes_at_kstep_boundaries(moe):
+    # top-1 routing that gives the experts 31, 32, 33, 64, 65, 96, 97, 1 and 0
+    # rows: groups ending just before, at and just after the 32- and 64-row
+    # K-steps of the weight-gradient loops, a one-row group and an empty one
+    sizes = [31, 32, 33, 64, 65, 96, 97, 1, 0]
+    E, d, f, k = len(sizes), 256, 256, 1
+    T = sum(sizes)
+    _say("layer-kstep-boundaries", sizes)
+    inp = moe_synth.make_inputs(T=T, d=d, E=E, f=f, k=k, seed=77)
+    owner = np.repeat(np.arange(E), sizes)
+    np.random.default_rng(5).shuffle(owner)
+    logits = inp["logits"].clone()
+    logits[torch.arange(T), torch.from_numpy(owner)] += 1e4   # each token's expert
+    inp["logits"] = logits
+    lay = _run_layer(moe, inp, k, "bf16", 0)
+    ref = oracle_layer(inp, k, capacity=0, round_mode=oracle.BF16)
+    _check_route(lay, ref["route"])
+    np.testing.assert_array_equal(lay.counts.cpu().numpy(), np.array(sizes))
+    assert_close(np64(lay.dx), ref["dx"], BF16_TOL, "dx")
+    assert_close(np64(lay.dw13), ref["dw13"], BF16_TOL, "dw13")
+    assert_close(np64(lay.dw2), ref["dw2"], BF16_TOL, "dw2")
+    for e, n in enumerate(sizes):
+        if n == 0:
+            continue
+        # every expert's gradient on its own scale, so a small group cannot hide
+        assert_close(np64(lay.dw13[e]), ref["dw13"][e], BF16_TOL, f"dw13[{e}]")
+        assert_close(np64(lay.dw2[e]), ref["dw2"][e], BF16_TOL, f"dw2[{e}]")
+    assert torch.all(lay.dw13[E - 1] == 0) and torch.all(lay.dw2[E - 1] == 0)
+
+
 @pytest.mark.parametrize("T,d,E,f,k,C", [(384, 256, 5, 384, 2, 0), (400, 128, 8, 128, 2, 70),
                                          (1100, 256, 4, 256, 1, 0)])
 def test_wgrad_fp32_accumulate(moe, T, d, E, f, k, C):
