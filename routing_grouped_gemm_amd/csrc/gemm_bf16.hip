@@ -821,7 +821,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_kernel(KParams p)
 //     group bounds come from a copy in LDS made at the start;
 //   - the next tile's first two K-steps go out to stages 0 and 1 before the
 //     current tile's epilogue, whose latency then hides under the epilogue;
-//   - the epilogue stages the result in stages 2 and 3, 128 rows at a time,
+//   - the epilogue stages the result in stages 2 and 3, 128 columns at a time,
 //     and leaves through 16 buffer stores per wave that are always issued
 //     (out of range elements are dropped by the buffer's range), so the next
 //     tile waits for the stores only from its third K-step on and they drain
@@ -834,7 +834,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_persistent(KParams p
 {
     constexpr int BM = 256, BK = 32, NS = 4, PRE = 2;
     constexpr int STAGE = (BM + BN) * BK;           // elements per stage
-    static_assert(2 * STAGE * 2 == 128 * BN * 2, "stages 2 and 3 hold 128 staged output rows");
+    static_assert(2 * STAGE * 2 == BM * 128 * 2, "stages 2 and 3 hold 128 staged output columns");
     __shared__ __align__(16) uint16_t smem[NS * STAGE];
     __shared__ int s_pos[2];
     __shared__ int64_t s_gb[kMaxExperts + 1];       // group bounds
@@ -941,8 +941,8 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_persistent(KParams p
         uint16_t* Ct = q.C + (int64_t)cur.e * q.sC + (int64_t)cur.mt * BM * q.ldc;
         const int rows = q.M - cur.mt * BM;
         uint8_t* stage23 = reinterpret_cast<uint8_t*>(smem + 2 * STAGE);
-        store_half_nt<NW>(acc, Ct, q.ldc, rows, cur.nt * BN, q.N, stage23, 0);
-        store_half_nt<NW>(acc, Ct, q.ldc, rows, cur.nt * BN, q.N, stage23, 1);
+        store_colhalf_nt<NW, 0>(acc, Ct, q.ldc, rows, cur.nt * BN, q.N, stage23);
+        store_colhalf_nt<NW, 1>(acc, Ct, q.ldc, rows, cur.nt * BN, q.N, stage23);
         if (Ln >= total) return;
         cur = nxt;
         stores16 = true;

@@ -709,50 +709,50 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[BM / 64][WL<NW>::
     });
 }
 
-// Rows [128 pass, 128 pass + 128) of a 256 x 256 accumulator tile (the
-// waves with wm == pass hold them) as bf16 rows of C: staged through the 64 KB
-// at lds, then 8 non-temporal 16-byte buffer stores per thread, always
+// Columns [128 PASS, 128 PASS + 128) of a 256 x 256 accumulator tile (sub-tile
+// j = PASS of every wave) as bf16 rows of C: staged through the 64 KB at lds
+// as 256 rows x 128 columns, then 8 non-temporal 16-byte buffer stores per
+// thread, a wave instruction covering 4 rows x 256 contiguous bytes, always
 // issued: an element outside rows x (N - col0) gets an offset past the
 // buffer's range and the hardware drops it.  Ct is row 0, column 0 of the
 // tile (wave-uniform) and every in-range byte offset (row * ldc + col) * 2 is
-// below 2^31.  A barrier before the LDS reads and one after them.
-template <int NW>
-__device__ __forceinline__ void store_half_nt(const f32x16 (&acc)[4][WL<NW>::NJ], uint16_t* Ct, int64_t ldc,
-                                              int rows, int col0, int N, uint8_t* lds, int pass)
+// below 2^31.  A barrier before the LDS reads and one after them.  Every wave
+// converts and stages in both passes (splitting the rows instead left half of
+// the waves idle while the other half staged: 1.3% slower weight gradient).
+template <int NW, int PASS>
+__device__ __forceinline__ void store_colhalf_nt(const f32x16 (&acc)[4][WL<NW>::NJ], uint16_t* Ct, int64_t ldc,
+                                                 int rows, int col0, int N, uint8_t* lds)
 {
+    static_assert(NW == 8, "sub-tile j of every wave is one 128-column half");
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(Ct, (short)0, 0x7fffffff, 0x00020000);
     constexpr int NT = WL<NW>::NT;
-    constexpr int PER = 128 * 32 / NT;            // 16-byte chunks per thread
+    constexpr int PER = 256 * 16 / NT;            // 16-byte chunks per thread
     // the thread index through an empty asm: the offsets below are then
     // computed here rather than hoisted out of a caller's tile loop
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int wm = WL<NW>::wm(wave), wn = WL<NW>::wn(wave);
-    if (wm == pass) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < WL<NW>::NJ; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    stage_put(lds, stage_off<32>(i * 32 + (lane & 31), acc_col<NW>(wn, j, g, lane)),
-                              pack4_bf16(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                         acc[i][j][4 * g + 3]));
-    }
+        for (int g = 0; g < 4; ++g)
+            stage_put(lds, stage_off<16>(wm * 128 + i * 32 + (lane & 31), wn * 32 + 8 * g + 4 * (lane >> 5)),
+                      pack4_bf16(acc[i][PASS][4 * g], acc[i][PASS][4 * g + 1], acc[i][PASS][4 * g + 2],
+                                 acc[i][PASS][4 * g + 3]));
     __syncthreads();
     uint4 v[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int q = tid + i * NT;
-        const int r = q >> 5, c = q & 31;
-        v[i] = *reinterpret_cast<const uint4*>(lds + r * 512 + ((c ^ (r & 31)) << 4));
+        const int r = q >> 4, c = q & 15;
+        v[i] = *reinterpret_cast<const uint4*>(lds + r * 256 + ((c ^ (r & 15)) << 4));
     }
     typedef __attribute__((ext_vector_type(4))) uint32_t vu4;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int q = tid + i * NT;
-        const int r = 128 * pass + (q >> 5), n = col0 + 8 * (q & 31);
+        const int r = q >> 4, n = col0 + PASS * 128 + 8 * (q & 15);
         const uint32_t off = r < rows && n < N ? (uint32_t)((r * ldc + n) * 2) : kOOB;
         __builtin_amdgcn_raw_buffer_store_b128(vu4{v[i].x, v[i].y, v[i].z, v[i].w}, rsrc, (int)off, 0,
                                                2 /* non-temporal */);
