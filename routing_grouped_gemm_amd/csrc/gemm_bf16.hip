@@ -122,7 +122,7 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
     constexpr int SM = MI * NJ;                    // MFMAs per k-slice
     constexpr int SPN = (NS == 2 ? kLoadSpan : kLoadSpanRing) * KS * SM / 32;
     constexpr int SPAN = SPN < NQ ? NQ : SPN;
-    static_assert(NS >= 2 && (NS & (NS - 1)) == 0, "a power-of-two ring of LDS stages");
+    static_assert(NS >= 2, "a ring of at least two LDS stages");
     static_assert(NS == 2 || KAL || (A_MN && B_MN), "deeper rings issue loads without the K-tail test");
     static_assert(PRE >= 0 && PRE < NS, "pre-issued K-steps fit the ring");
     static_assert(KS >= 2 && KS % 2 == 0, "an even number of k-slices per K-step");
@@ -222,14 +222,14 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
         if (PRE > 0 && stores16 && kt < PRE) wait_vmcnt<NQ * (NS - 2) + 16>();
         else wait_vmcnt<NQ * (NS - 2)>();
         __syncthreads();     // everyone's have, and the stage loaded next is no longer read
-        int so = (kt & (NS - 1)) * STAGE;
+        int so = (kt % NS) * STAGE;
         // one stage base in a scalar register, rather than per-stage copies
         // of every fragment address kept live across the loop
         if constexpr (NS > 2) asm volatile("" : "+s"(so));
         const uint16_t* a_s = smem + so;
         const uint16_t* b_s = a_s + BM * BK;
         const int kn = kt + NS - 1;                                      // the K-step loaded now
-        const uint32_t nso = (uint32_t)((kn & (NS - 1)) * STAGE * 2);    // its stage, bytes
+        const uint32_t nso = (uint32_t)((kn % NS) * STAGE * 2);          // its stage, bytes
         auto load = [&](int q) __attribute__((always_inline)) {
             if constexpr (md == 1 && NS > 2) {
                 if (q < NA) la.issue_ring(nso, kn, q, kn < nk);
@@ -600,10 +600,22 @@ __device__ __forceinline__ void mainloop_pp(const TileSrc& sa, const TileSrc& sb
 
 // Grouped-M GEMM: C[rows of group e] = A[rows of group e] x B_e^T (B_MN = false:
 // B_e stored [N, K]) or A x B_e (B_MN = true: B_e stored [K, N]).
+// LDS stages of the main loop of a BMS-row tail tile (K a multiple of 64):
+// a 64-row K-step is 512 MFMA cycles per SIMD against 40 KB of loads, so two
+// stages left it waiting on the load latency most of the time (a 64-row
+// tail took 80% of a full tile's time); four stages of 40 KB fill the 160 KB
+// of LDS and keep three K-steps of loads in flight, three of 48 KB two.
+template <int BMS>
+constexpr int tail_stages() { return BMS == 64 ? 4 : 3; }
+
 template <int BM, int BK, int NS, bool B_MN, int EPI, int NW, bool KAL>
 __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_m_kernel(MParams p)
 {
-    __shared__ __align__(16) uint16_t smem[NS * (BM + BN) * BK];
+    constexpr int SMEM = KAL && BM == 256 && BK == 64 ? tail_stages<64>() * (64 + BN) * BK : NS * (BM + BN) * BK;
+    static_assert(SMEM >= NS * (BM + BN) * BK, "LDS for the full-tile loop");
+    static_assert(!(KAL && BM == 256 && BK == 64) || SMEM >= tail_stages<128>() * (128 + BN) * BK,
+                  "LDS for the tail-tile rings");
+    __shared__ __align__(16) uint16_t smem[SMEM];
 
     // device tile schedule: expert-major, N-tile, then M-tile
     MTile tile;
@@ -653,7 +665,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_m_kernel(MParams p)
             st.rows0 = min(rows_valid, BMS / 2);
             st.rows1 = max(rows_valid - BMS / 2, 0);
             f32x16 acc_s[BMS / 64][WL<NW>::NJ];
-            mainloop<BMS, BK, NS, false, B_MN, NW, KAL>(st, sb, acc_s, smem);
+            mainloop<BMS, BK, KAL ? tail_stages<BMS>() : NS, false, B_MN, NW, KAL>(st, sb, acc_s, smem);
             epilogue_m<BMS, EPI, NW>(acc_s, p, row0, rows_valid, nt, reinterpret_cast<uint8_t*>(smem));
         };
         if (rows_valid <= 64) {
