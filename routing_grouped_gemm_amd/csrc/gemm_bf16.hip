@@ -617,7 +617,8 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_m_kernel(MParams p)
                   "LDS for the tail-tile rings");
     __shared__ __align__(16) uint16_t smem[SMEM];
 
-    // device tile schedule: expert-major, N-tile, then M-tile
+    // device tile schedule: expert-major, then groups of M-tiles (N-tiles
+    // across a group, M-tiles fastest within)
     MTile tile;
     if (!schedule_m<BM>(p.group_off, p.capacity, p.E, p.n_rows, p.ntn, tile)) return;
     const int e = tile.e, nt = tile.nt;

@@ -579,12 +579,33 @@ __device__ __forceinline__ void epilogue_m(const f32x16 (&acc)[BM / 64][WL<NW>::
                                                amdgpu_flat_work_group_size(64 * (NW), 64 * (NW))))
 
 
+// Tile (mt, nt) of the local-th tile of an mtn x ntn grid, walked in groups
+// of GM tile rows (nt fastest across a group's columns, mt fastest within):
+// a run of consecutive tiles then shares GM row slices of A and a few column
+// slices of B, which stay in L2 while those tiles run together.
+__device__ __forceinline__ void grouped_tile(int local, int mtn, int ntn, int GM, int& mt, int& nt)
+{
+    const int per_group = GM * ntn;
+    const int g = local / per_group;
+    const int first = g * GM;
+    const int gm = min(mtn - first, GM);
+    const int r = local - g * per_group;
+    mt = first + r % gm;
+    nt = r / gm;
+}
+
 // Device tile schedule of a grouped-M launch: every wave of a workgroup
 // sums, lane by lane, the ceil(m_e / BM) * ntn tiles of the experts (lane l
 // takes experts l*per .. l*per+per-1, per = ceil(E / 64)) and scans the lane
 // sums across the wave (no LDS, no barrier), remaps the workgroup id so
 // that a contiguous range of tiles lands on one XCD, and finds its expert,
 // N-tile and M-tile.  Returns false for surplus workgroups.
+// An expert's tiles go in groups of kMTileGroup M-tiles (N-tiles across a
+// group, M-tiles fastest within): the 32 tiles an XCD runs at once then read
+// a few M-slices of A and N-slices of B (with all of a large expert's M-tiles
+// per N-tile, 32 concurrent tiles would read 32 A slices and one B slice).
+constexpr int kMTileGroup = 4;
+
 struct MTile {
     int e, nt, mt, rows_valid;
     int64_t row0;
@@ -632,26 +653,10 @@ __device__ __forceinline__ bool schedule_m(const int32_t* group_off, int capacit
     const int64_t g0 = group_begin(group_off, capacity, t.e, n_rows);
     const int m_e = (int)group_rows(group_off, capacity, t.e, n_rows);
     const int mt_e = (m_e + BM - 1) / BM;
-    t.nt = local / mt_e;
-    t.mt = local - t.nt * mt_e;
+    grouped_tile(local, mt_e, ntn, kMTileGroup, t.mt, t.nt);
     t.row0 = g0 + (int64_t)t.mt * BM;
     t.rows_valid = min(BM, m_e - t.mt * BM);
     return true;
-}
-
-// Tile (mt, nt) of the local-th tile of an mtn x ntn grid, walked in groups
-// of GM tile rows (nt fastest across a group's columns, mt fastest within):
-// a run of consecutive tiles then shares GM row slices of A and a few column
-// slices of B, which stay in L2 while those tiles run together.
-__device__ __forceinline__ void grouped_tile(int local, int mtn, int ntn, int GM, int& mt, int& nt)
-{
-    const int per_group = GM * ntn;
-    const int g = local / per_group;
-    const int first = g * GM;
-    const int gm = min(mtn - first, GM);
-    const int r = local - g * per_group;
-    mt = first + r % gm;
-    nt = r / gm;
 }
 
 // add a BM x 256 accumulator tile into fp32 rows of C (rows [0, rows),
