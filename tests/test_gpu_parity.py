@@ -218,6 +218,36 @@ def test_layer_group_sizes_at_kstep_boundaries(moe):
     assert torch.all(lay.dw13[E - 1] == 0) and torch.all(lay.dw2[E - 1] == 0)
 
 
+def test_layer_large_groups_partial_mtile_groups(moe):
+    # top-1 routing with experts of 1300, 0, 2050 and 700 rows: 6, 0, 9 and 3
+    # M-tiles, so the grouped-M tile order (groups of four M-tiles, N-tiles
+    # across a group) ends on partial groups of 2 and 1 M-tiles, with 3 N-tiles
+    # at gate/up, 2 (one partial) at dgrad-down and 1 at down / dgrad-gate/up
+    sizes = [1300, 0, 2050, 700]
+    E, d, f, k = len(sizes), 256, 384, 1
+    T = sum(sizes)
+    _say("layer-partial-mtile-groups", sizes)
+    inp = moe_synth.make_inputs(T=T, d=d, E=E, f=f, k=k, seed=91)
+    owner = np.repeat(np.arange(E), sizes)
+    np.random.default_rng(9).shuffle(owner)
+    logits = inp["logits"].clone()
+    logits[torch.arange(T), torch.from_numpy(owner)] += 1e4   # each token's expert
+    inp["logits"] = logits
+    lay = _run_layer(moe, inp, k, "bf16", 0)
+    ref = oracle_layer(inp, k, capacity=0, round_mode=oracle.BF16)
+    _check_route(lay, ref["route"])
+    np.testing.assert_array_equal(lay.counts.cpu().numpy(), np.array(sizes))
+    assert_close(np64(lay.h), ref["h"], BF16_TOL, "h")
+    assert_close(np64(lay.out), ref["out"], BF16_TOL, "out")
+    assert_close(np64(lay.dx), ref["dx"], BF16_TOL, "dx")
+    for e, n in enumerate(sizes):
+        if n == 0:
+            assert torch.all(lay.dw13[e] == 0) and torch.all(lay.dw2[e] == 0)
+            continue
+        assert_close(np64(lay.dw13[e]), ref["dw13"][e], BF16_TOL, f"dw13[{e}]")
+        assert_close(np64(lay.dw2[e]), ref["dw2"][e], BF16_TOL, f"dw2[{e}]")
+
+
 @pytest.mark.parametrize("T,d,E,f,k,C", [(384, 256, 5, 384, 2, 0), (400, 128, 8, 128, 2, 70),
                                          (1100, 256, 4, 256, 1, 0)])
 def test_wgrad_fp32_accumulate(moe, T, d, E, f, k, C):
