@@ -842,7 +842,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_kernel(KParams p)
 //     while none computes.  (Storing from the accumulators without LDS, 32
 //     bytes of each of 32 rows per instruction, measured 3.1 ms against
 //     2.8 ms at e128 with plain stores and 6.6 ms non-temporal.)
-template <int NW>
+template <int NW, bool F32 = false>
 __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_persistent(KParams p)
 {
     constexpr int BM = 256, BK = 32, NS = 4, PRE = 2;
@@ -951,14 +951,21 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_persistent(KParams p
             first_loads(nxt);
         }
         const KProblem& q = cur.which ? p.pr[1] : p.pr[0];
-        uint16_t* Ct = q.C + (int64_t)cur.e * q.sC + (int64_t)cur.mt * BM * q.ldc;
         const int rows = q.M - cur.mt * BM;
         uint8_t* stage23 = reinterpret_cast<uint8_t*>(smem + 2 * STAGE);
-        store_colhalf_nt<NW, 0>(acc, Ct, q.ldc, rows, cur.nt * BN, q.N, stage23);
-        store_colhalf_nt<NW, 1>(acc, Ct, q.ldc, rows, cur.nt * BN, q.N, stage23);
+        if constexpr (F32) {
+            // added into fp32 accumulators (64 loads and stores per thread:
+            // the next tile's first K-steps wait for them, stores16 stays off)
+            add_tile_f32_rows<NW>(acc, q.Cf + (int64_t)cur.e * q.sC + (int64_t)cur.mt * BM * q.ldc, q.ldc, rows,
+                                  cur.nt * BN, q.N, stage23);
+        } else {
+            uint16_t* Ct = q.C + (int64_t)cur.e * q.sC + (int64_t)cur.mt * BM * q.ldc;
+            store_colhalf_nt<NW, 0>(acc, Ct, q.ldc, rows, cur.nt * BN, q.N, stage23);
+            store_colhalf_nt<NW, 1>(acc, Ct, q.ldc, rows, cur.nt * BN, q.N, stage23);
+        }
         if (Ln >= total) return;
         cur = nxt;
-        stores16 = true;
+        stores16 = !F32;
     }
 }
 
@@ -1103,13 +1110,19 @@ hipError_t launch_k(const KParams& p, hipStream_t s)
     const int64_t grid = (total + 8 * kKDealRun - 1) / (8 * kKDealRun) * (8 * kKDealRun);
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL(k_deal_flag_kernel, dim3(1), dim3(64), 0, s, p, (int)tiles_e, (int)((total + 7) / 8));
-    // the persistent kernel for bf16 outputs whose tile offsets fit its 31-bit buffer range
-    bool persistent = BM == 256 && BK == 64 && NS == 2 && NW == 8;
-    for (int i = 0; i < p.nprob; ++i)
+    // the persistent kernel: for bf16 outputs whose tile offsets fit its
+    // 31-bit buffer range, or (its fp32 form) when every problem adds into
+    // fp32 accumulators
+    bool persistent = BM == 256 && BK == 64 && NS == 2 && NW == 8, all_f32 = true;
+    for (int i = 0; i < p.nprob; ++i) {
+        all_f32 = all_f32 && p.pr[i].Cf;
         persistent = persistent && !p.pr[i].Cf && (int64_t)256 * p.pr[i].ldc * 2 < ((int64_t)1 << 31);
+    }
+    const int64_t pgrid = std::min<int64_t>(persistent_grid(), (total + 7) / 8 * 8);
     if (persistent) {
-        const int64_t pgrid = std::min<int64_t>(persistent_grid(), (total + 7) / 8 * 8);
         hipLaunchKernelGGL((gemm_grouped_k_persistent<NW>), dim3((unsigned)pgrid), dim3(64 * NW), 0, s, p);
+    } else if (all_f32 && BM == 256 && BK == 64 && NS == 2 && NW == 8) {
+        hipLaunchKernelGGL((gemm_grouped_k_persistent<NW, true>), dim3((unsigned)pgrid), dim3(64 * NW), 0, s, p);
     } else {
         hipLaunchKernelGGL((gemm_grouped_k_kernel<BM, BK, NS, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, p);
     }

@@ -664,8 +664,10 @@ __device__ __forceinline__ bool schedule_m(const int32_t* group_off, int capacit
 // from the accumulator layout: each lane reads, adds and writes back its
 // four consecutive columns of one row, 32 rows at a time (all of a 32-row
 // block's reads before its writes).  Staging the fp32 tile through the LDS
-// for whole-row accesses measured no faster: the read-modify-write of the
-// tile is bound by the HBM traffic of the tiles finishing together.
+// for whole-row accesses measured no faster in the one-workgroup-per-tile
+// kernel, where the tiles finish together and the read-modify-write is bound
+// by their simultaneous HBM traffic (the persistent walk, whose tiles finish
+// at different times, uses the staged form below).
 template <int BM, int NW>
 __device__ __forceinline__ void add_tile_f32(const f32x16 (&acc)[BM / 64][WL<NW>::NJ], float* C, int64_t ldc,
                                              int rows, int col0, int N)
@@ -763,6 +765,61 @@ __device__ __forceinline__ void store_colhalf_nt(const f32x16 (&acc)[4][WL<NW>::
                                                2 /* non-temporal */);
     }
     __syncthreads();
+}
+
+// A 256 x 256 accumulator tile added into fp32 rows of C, in four passes of
+// 64 tile rows: pass i is accumulator sub-tile i of every wave (rows 32i ..
+// 32i + 31 and 128 + 32i .. 128 + 32i + 31), staged through the 64 KB at lds
+// as 64 rows x 256 fp32 (16-byte chunk c of staged row r at chunk c ^ (r & 63),
+// so both the accumulator-layout writes and the row reads spread over the
+// banks).  Every thread first loads its 8 chunks of C for the pass (a wave
+// instruction covers one row's 1 KB), then the tile is staged, and after a
+// barrier each thread adds its chunks and stores them back in place; a barrier
+// frees the LDS for the next pass.  C is row 0, column 0 of the tile; rows and
+// columns outside rows x (N - col0) are skipped (N % 4 == 0).
+template <int NW>
+__device__ __forceinline__ void add_tile_f32_rows(const f32x16 (&acc)[4][WL<NW>::NJ], float* C, int64_t ldc,
+                                                  int rows, int col0, int N, uint8_t* lds)
+{
+    static_assert(NW == 8, "sub-tile i of every wave is one 64-row pass");
+    constexpr int NT = WL<NW>::NT;
+    constexpr int PER = 64 * 64 / NT;             // 16-byte chunks per thread and pass
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));                 // offsets computed here, not hoisted out of the tile loop
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int wm = WL<NW>::wm(wave), wn = WL<NW>::wn(wave);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // this thread's chunks: staged row (wave + 8n), chunk lane
+        auto tile_row = [&](int pr) __attribute__((always_inline)) { return (pr < 32 ? 0 : 128 - 32) + i * 32 + pr; };
+        float4 cv[PER];
+#pragma unroll
+        for (int n = 0; n < PER; ++n) {
+            const int tr = tile_row(wave + 8 * n), col = col0 + 4 * lane;
+            cv[n] = tr < rows && col < N ? *reinterpret_cast<const float4*>(C + tr * ldc + col)
+                                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < WL<NW>::NJ; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int pr = wm * 32 + (lane & 31);
+                const int c = (WL<NW>::sub_col(wn, j) + 8 * g + 4 * (lane >> 5)) >> 2;
+                *reinterpret_cast<float4*>(lds + pr * 1024 + ((c ^ (pr & 63)) << 4)) =
+                    make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+            }
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < PER; ++n) {
+            const int pr = wave + 8 * n;
+            const float4 a = *reinterpret_cast<const float4*>(lds + pr * 1024 + ((lane ^ (pr & 63)) << 4));
+            const int tr = tile_row(pr), col = col0 + 4 * lane;
+            if (tr < rows && col < N)
+                *reinterpret_cast<float4*>(C + tr * ldc + col) =
+                    make_float4(cv[n].x + a.x, cv[n].y + a.y, cv[n].z + a.z, cv[n].w + a.w);
+        }
+        __syncthreads();
+    }
 }
 
 }  // namespace gemm
