@@ -102,10 +102,11 @@ __device__ __forceinline__ bf16x8 read_frag(const uint16_t* tile, int row_base, 
 // that they cover the latency of the first fragment reads of the new K-step.
 // PRE: K-steps 0 .. PRE-1 were already issued into stages 0 .. PRE-1 by the
 // caller (with loaders made from the same sources); stores16: the caller
-// issued exactly 16 vector memory operations per wave after those loads (and
-// nothing else since), so they are waited for only from K-step PRE on and
-// may drain during the first K-steps.
-template <int BM, int BK, int NS, bool A_MN, bool B_MN, int NW, bool KAL, int PRE = 0>
+// issued at least NDRAIN vector memory operations per wave after those loads
+// (exactly 16 stores for the bf16 epilogue; 64 loads and stores, the last 8
+// of them stores, for the fp32 one), so the last NDRAIN are waited for only
+// from K-step PRE on and may drain during the first K-steps.
+template <int BM, int BK, int NS, bool A_MN, bool B_MN, int NW, bool KAL, int PRE = 0, int NDRAIN = 16>
 __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
                                          f32x16 (&acc)[BM / 64][WL<NW>::NJ], uint16_t* smem,
                                          bool stores16 = false)
@@ -219,7 +220,7 @@ __device__ __forceinline__ void mainloop(const TileSrc& sa, const TileSrc& sb,
         constexpr int md = decltype(MODE)::value;
         // this wave's loads of K-step kt have landed (those of the NS - 2
         // K-steps after it, and stores the caller issued after them, may not)
-        if (PRE > 0 && stores16 && kt < PRE) wait_vmcnt<NQ * (NS - 2) + 16>();
+        if (PRE > 0 && stores16 && kt < PRE) wait_vmcnt<NQ * (NS - 2) + NDRAIN>();
         else wait_vmcnt<NQ * (NS - 2)>();
         __syncthreads();     // everyone's have, and the stage loaded next is no longer read
         int so = (kt % NS) * STAGE;
@@ -941,7 +942,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_persistent(KParams p
         TileSrc sa, sb;
         sources(cur, sa, sb);
         f32x16 acc[BM / 64][WL<NW>::NJ];
-        mainloop<BM, BK, NS, true, true, NW, true, PRE>(sa, sb, acc, smem, stores16);
+        mainloop<BM, BK, NS, true, true, NW, true, PRE, F32 ? 8 : 16>(sa, sb, acc, smem, stores16);
         if (threadIdx.x == 0) s_pos[it & 1] = pos;
         __syncthreads();
         const int Ln = tile_at(s_pos[it & 1]);
@@ -954,8 +955,9 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_persistent(KParams p
         const int rows = q.M - cur.mt * BM;
         uint8_t* stage23 = reinterpret_cast<uint8_t*>(smem + 2 * STAGE);
         if constexpr (F32) {
-            // added into fp32 accumulators (64 loads and stores per thread:
-            // the next tile's first K-steps wait for them, stores16 stays off)
+            // added into fp32 accumulators: 64 loads and stores per thread,
+            // always issued; the last pass's 8 stores drain under the next
+            // tile's first K-steps
             add_tile_f32_rows<NW>(acc, q.Cf + (int64_t)cur.e * q.sC + (int64_t)cur.mt * BM * q.ldc, q.ldc, rows,
                                   cur.nt * BN, q.N, stage23);
         } else {
@@ -965,7 +967,7 @@ __global__ MOE_GEMM_KERNEL_ATTRS_NW(NW) void gemm_grouped_k_persistent(KParams p
         }
         if (Ln >= total) return;
         cur = nxt;
-        stores16 = !F32;
+        stores16 = true;
     }
 }
 
@@ -1112,11 +1114,12 @@ hipError_t launch_k(const KParams& p, hipStream_t s)
     hipLaunchKernelGGL(k_deal_flag_kernel, dim3(1), dim3(64), 0, s, p, (int)tiles_e, (int)((total + 7) / 8));
     // the persistent kernel: for bf16 outputs whose tile offsets fit its
     // 31-bit buffer range, or (its fp32 form) when every problem adds into
-    // fp32 accumulators
+    // fp32 accumulators whose tile offsets fit it
     bool persistent = BM == 256 && BK == 64 && NS == 2 && NW == 8, all_f32 = true;
     for (int i = 0; i < p.nprob; ++i) {
         all_f32 = all_f32 && p.pr[i].Cf;
         persistent = persistent && !p.pr[i].Cf && (int64_t)256 * p.pr[i].ldc * 2 < ((int64_t)1 << 31);
+        all_f32 = all_f32 && (int64_t)256 * p.pr[i].ldc * 4 < ((int64_t)1 << 31);
     }
     const int64_t pgrid = std::min<int64_t>(persistent_grid(), (total + 7) / 8 * 8);
     if (persistent) {

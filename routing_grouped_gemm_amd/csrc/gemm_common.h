@@ -774,9 +774,12 @@ __device__ __forceinline__ void store_colhalf_nt(const f32x16 (&acc)[4][WL<NW>::
 // so both the accumulator-layout writes and the row reads spread over the
 // banks).  Every thread first loads its 8 chunks of C for the pass (a wave
 // instruction covers one row's 1 KB), then the tile is staged, and after a
-// barrier each thread adds its chunks and stores them back in place; a barrier
-// frees the LDS for the next pass.  C is row 0, column 0 of the tile; rows and
-// columns outside rows x (N - col0) are skipped (N % 4 == 0).
+// barrier each thread adds its chunks and stores them back in place
+// (non-temporal); a barrier frees the LDS for the next pass.  Every load and
+// store is issued, 64 per thread, whatever the tile's extent: a chunk outside
+// rows x (N - col0) gets an offset past the buffer's range (the load returns
+// zeros, the store is dropped).  C is row 0, column 0 of the tile
+// (wave-uniform), every in-range byte offset below 2^31, N % 4 == 0.
 template <int NW>
 __device__ __forceinline__ void add_tile_f32_rows(const f32x16 (&acc)[4][WL<NW>::NJ], float* C, int64_t ldc,
                                                   int rows, int col0, int N, uint8_t* lds)
@@ -784,6 +787,8 @@ __device__ __forceinline__ void add_tile_f32_rows(const f32x16 (&acc)[4][WL<NW>:
     static_assert(NW == 8, "sub-tile i of every wave is one 64-row pass");
     constexpr int NT = WL<NW>::NT;
     constexpr int PER = 64 * 64 / NT;             // 16-byte chunks per thread and pass
+    typedef __attribute__((ext_vector_type(4))) uint32_t vu4;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(C, (short)0, 0x7fffffff, 0x00020000);
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));                 // offsets computed here, not hoisted out of the tile loop
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -791,14 +796,13 @@ __device__ __forceinline__ void add_tile_f32_rows(const f32x16 (&acc)[4][WL<NW>:
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         // this thread's chunks: staged row (wave + 8n), chunk lane
-        auto tile_row = [&](int pr) __attribute__((always_inline)) { return (pr < 32 ? 0 : 128 - 32) + i * 32 + pr; };
-        float4 cv[PER];
+        auto offset = [&](int pr) __attribute__((always_inline)) {
+            const int tr = (pr < 32 ? 0 : 128 - 32) + i * 32 + pr, col = col0 + 4 * lane;
+            return tr < rows && col < N ? (uint32_t)((tr * ldc + col) * 4) : kOOB;
+        };
+        vu4 cv[PER];
 #pragma unroll
-        for (int n = 0; n < PER; ++n) {
-            const int tr = tile_row(wave + 8 * n), col = col0 + 4 * lane;
-            cv[n] = tr < rows && col < N ? *reinterpret_cast<const float4*>(C + tr * ldc + col)
-                                         : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+        for (int n = 0; n < PER; ++n) cv[n] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)offset(wave + 8 * n), 0, 0);
 #pragma unroll
         for (int j = 0; j < WL<NW>::NJ; ++j)
 #pragma unroll
@@ -813,10 +817,9 @@ __device__ __forceinline__ void add_tile_f32_rows(const f32x16 (&acc)[4][WL<NW>:
         for (int n = 0; n < PER; ++n) {
             const int pr = wave + 8 * n;
             const float4 a = *reinterpret_cast<const float4*>(lds + pr * 1024 + ((lane ^ (pr & 63)) << 4));
-            const int tr = tile_row(pr), col = col0 + 4 * lane;
-            if (tr < rows && col < N)
-                *reinterpret_cast<float4*>(C + tr * ldc + col) =
-                    make_float4(cv[n].x + a.x, cv[n].y + a.y, cv[n].z + a.z, cv[n].w + a.w);
+            const vu4 o = {__float_as_uint(__uint_as_float(cv[n].x) + a.x), __float_as_uint(__uint_as_float(cv[n].y) + a.y),
+                           __float_as_uint(__uint_as_float(cv[n].z) + a.z), __float_as_uint(__uint_as_float(cv[n].w) + a.w)};
+            __builtin_amdgcn_raw_buffer_store_b128(o, rsrc, (int)offset(pr), 0, 2 /* non-temporal */);
         }
         __syncthreads();
     }
