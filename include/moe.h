@@ -257,7 +257,7 @@ typedef struct moe_gemm_tensors {
     void* dx_perm;               /* [n_rows, d]                     */
     void* dw13;                  /* [E, 2f, d]                      */
     void* dw2;                   /* [E, d, f]                       */
-    void* ws;                    /* MOE_MXFP8 workspace             */
+    void* ws;                    /* workspace (MXFP8 stages, bf16 WGRAD) */
     size_t ws_bytes;
     /* MOE_BF16 WGRAD only, optional (both or neither): fp32 weight-gradient
      * accumulators [E, 2f, d] and [E, d, f].  When set, WGRAD adds its sums
