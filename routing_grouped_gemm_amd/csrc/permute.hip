@@ -43,14 +43,38 @@ __device__ __forceinline__ uint4 scale_vec(uint4 v, float s)
 
 // thread i handles vector (i % nvec) of token row (i / nvec).  K (= top-k)
 // is a template parameter: the token's K destinations and scales are read
-// first, then its K stores go out back to back.
-template <bool BF16, bool SCALE, int K>
+// first, then its K stores go out back to back.  ROW (rows of at least 256
+// vectors): one workgroup per token, each thread its vectors tid, tid + 256,
+// ...; the destinations and scales are then workgroup-uniform (scalar loads,
+// once per token instead of once per vector).
+template <bool BF16, bool SCALE, int K, bool ROW = false>
 __global__ __launch_bounds__(256) void permute_kernel(const uint4* __restrict__ x, int T, int nvec,
                                                       const int32_t* __restrict__ dst_row,
                                                       const float* __restrict__ row_scale,
                                                       int64_t n_rows, uint4* __restrict__ x_perm,
                                                       int32_t* __restrict__ dev_err)
 {
+    if constexpr (ROW) {
+        const int64_t t = blockIdx.x;
+        int32_t dst[K];
+        float sc[K];
+        bool bad = false;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            dst[j] = dst_row[t * K + j];
+            sc[j] = SCALE ? row_scale[t * K + j] : 1.0f;
+            bad |= dst[j] >= n_rows;
+        }
+        for (int v = threadIdx.x; v < nvec; v += 256) {
+            const uint4 val = x[t * nvec + v];
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                if (dst[j] >= 0 && dst[j] < n_rows)
+                    x_perm[(int64_t)dst[j] * nvec + v] = SCALE ? scale_vec<BF16>(val, sc[j]) : val;
+        }
+        if (bad && dev_err && threadIdx.x == 0) atomicOr(dev_err, (int)MOE_ERR_ROW_RANGE);
+        return;
+    }
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)T * nvec) return;
     const int64_t t = i / nvec;
@@ -340,20 +364,13 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const uint16_t* __restr
             *reinterpret_cast<const uint32_t*>(s_osc + tid * 4);
 }
 
-// thread i makes vector (i % nvec) of token (i / nvec): the K destination
-// rows and weights are read first, then the K row loads are all in flight
-// before the fp32 accumulation in slot order.
+// vector v of token t of the combine (flag: this thread reports a row out of range)
 template <bool BF16, int K>
-__global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y,
-                                                      const int32_t* __restrict__ dst_row,
-                                                      const float* __restrict__ w, int T, int nvec,
-                                                      int64_t n_rows, uint4* __restrict__ out,
-                                                      int32_t* __restrict__ dev_err)
+__device__ __forceinline__ void combine_vec(const uint4* __restrict__ y, const int32_t* __restrict__ dst_row,
+                                            const float* __restrict__ w, int64_t t, int v, int nvec, int64_t n_rows,
+                                            uint4* __restrict__ out, int32_t* __restrict__ dev_err, bool flag)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)T * nvec) return;
-    const int64_t t = i / nvec;
-    const int v = (int)(i - t * nvec);
+    const int64_t i = t * nvec + v;
     constexpr int NE = BF16 ? 8 : 4;
     int32_t dst[K];
     float wt[K];
@@ -399,8 +416,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
                 __float_as_uint(acc[3])};
     }
     __builtin_nontemporal_store(o, reinterpret_cast<vu4*>(out) + i);
-    if (bad && dev_err) atomicOr(dev_err, (int)MOE_ERR_ROW_RANGE);
+    if (bad && dev_err && flag) atomicOr(dev_err, (int)MOE_ERR_ROW_RANGE);
 }
+
+// thread i makes vector (i % nvec) of token (i / nvec): the K destination
+// rows and weights are read first, then the K row loads are all in flight
+// before the fp32 accumulation in slot order.  ROW (rows of at least 256
+// vectors): one workgroup per token, each thread its vectors tid, tid + 256,
+// ... (workgroup-uniform destinations and weights: scalar loads).
+template <bool BF16, int K, bool ROW = false>
+__global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y,
+                                                      const int32_t* __restrict__ dst_row,
+                                                      const float* __restrict__ w, int T, int nvec,
+                                                      int64_t n_rows, uint4* __restrict__ out,
+                                                      int32_t* __restrict__ dev_err)
+{
+    if constexpr (ROW) {
+        for (int v = threadIdx.x; v < nvec; v += 256) combine_vec<BF16, K>(y, dst_row, w, blockIdx.x, v, nvec, n_rows, out,
+                                                                          dev_err, threadIdx.x == 0 && v == (int)threadIdx.x);
+        return;
+    }
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)T * nvec) return;
+    combine_vec<BF16, K>(y, dst_row, w, i / nvec, (int)(i - (i / nvec) * nvec), nvec, n_rows, out, dev_err, true);
+}
+
 
 // Gradient through the gate weights (the backward of the weighted combine
 // with respect to the weights, then the softmax over the selected logits):
@@ -529,21 +569,29 @@ hipError_t launch_permute(int dtype, const void* x, int T, int d, int k, const i
     const int nvec = bf ? d / 8 : d / 4;
     const int64_t n = (int64_t)T * nvec;
     if (n > 0) {
-        const dim3 grid(grid_for(n)), blk(256);
+        // rows of at least 256 vectors: one workgroup per token when a token
+        // has at most 2 slots, or for the row-scaled form (measured: 7-19%
+        // faster at k = 1 and 5% for the scaled copy at k = 4, 2% slower for
+        // the plain copy at k = 4)
+        const bool row = nvec >= 256 && (k <= 2 || row_scale);
+        const dim3 grid(row ? (unsigned)T : grid_for(n)), blk(256);
         const hipError_t e = with_k(k, [&](auto kc) {
             constexpr int K = decltype(kc)::value;
-            if (bf && row_scale)
-                hipLaunchKernelGGL((permute_kernel<true, true, K>), grid, blk, 0, s, (const uint4*)x, T, nvec,
-                                   dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
-            else if (bf)
-                hipLaunchKernelGGL((permute_kernel<true, false, K>), grid, blk, 0, s, (const uint4*)x, T, nvec,
-                                   dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
-            else if (row_scale)
-                hipLaunchKernelGGL((permute_kernel<false, true, K>), grid, blk, 0, s, (const uint4*)x, T, nvec,
-                                   dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
-            else
-                hipLaunchKernelGGL((permute_kernel<false, false, K>), grid, blk, 0, s, (const uint4*)x, T, nvec,
-                                   dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
+            auto go = [&](auto BF_, auto SC_) {
+                constexpr bool BF = decltype(BF_)::value, SC = decltype(SC_)::value;
+                if (row)
+                    hipLaunchKernelGGL((permute_kernel<BF, SC, K, true>), grid, blk, 0, s, (const uint4*)x, T, nvec,
+                                       dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
+                else
+                    hipLaunchKernelGGL((permute_kernel<BF, SC, K>), grid, blk, 0, s, (const uint4*)x, T, nvec,
+                                       dst_row, row_scale, n_rows, (uint4*)x_perm, dev_err);
+            };
+            using T_ = std::true_type;
+            using F_ = std::false_type;
+            if (bf && row_scale) go(T_{}, T_{});
+            else if (bf) go(T_{}, F_{});
+            else if (row_scale) go(F_{}, T_{});
+            else go(F_{}, F_{});
         });
         if (e != hipSuccess) return e;
     }
@@ -561,13 +609,23 @@ hipError_t launch_combine(int dtype, const void* y_perm, const int32_t* dst_row,
     const int nvec = bf ? d / 8 : d / 4;
     const int64_t n = (int64_t)T * nvec;
     if (n > 0) {
+        // rows of at least 256 vectors and at most 2 slots per token: one
+        // workgroup per token (11-19% faster at k = 1, 2-3.5% slower at k = 4)
+        const bool row = nvec >= 256 && k <= 2;
+        const dim3 grid(row ? (unsigned)T : grid_for(n));
         const hipError_t e = with_k(k, [&](auto kc) {
             constexpr int K = decltype(kc)::value;
-            if (bf)
-                hipLaunchKernelGGL((combine_kernel<true, K>), dim3(grid_for(n)), dim3(256), 0, s,
+            if (bf && row)
+                hipLaunchKernelGGL((combine_kernel<true, K, true>), grid, dim3(256), 0, s,
+                                   (const uint4*)y_perm, dst_row, w, T, nvec, n_rows, (uint4*)out, dev_err);
+            else if (bf)
+                hipLaunchKernelGGL((combine_kernel<true, K>), grid, dim3(256), 0, s,
+                                   (const uint4*)y_perm, dst_row, w, T, nvec, n_rows, (uint4*)out, dev_err);
+            else if (row)
+                hipLaunchKernelGGL((combine_kernel<false, K, true>), grid, dim3(256), 0, s,
                                    (const uint4*)y_perm, dst_row, w, T, nvec, n_rows, (uint4*)out, dev_err);
             else
-                hipLaunchKernelGGL((combine_kernel<false, K>), dim3(grid_for(n)), dim3(256), 0, s,
+                hipLaunchKernelGGL((combine_kernel<false, K>), grid, dim3(256), 0, s,
                                    (const uint4*)y_perm, dst_row, w, T, nvec, n_rows, (uint4*)out, dev_err);
         });
         if (e != hipSuccess) return e;

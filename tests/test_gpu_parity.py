@@ -142,6 +142,10 @@ LAYER_CASES = [
     (160, 128, 6, 128, 2, "bf16", 0),
     (1400, 256, 4, 256, 1, "bf16", 0),
     (600, 128, 1024, 64, 8, "bf16", 0),     # the most experts and slots: ~5 rows per expert
+    # rows of at least 256 16-byte vectors: permute and combine run one workgroup per token
+    (150, 2048, 8, 128, 2, "bf16", 0),
+    (130, 2056, 5, 64, 3, "bf16", 60),      # 257 vectors per row, padded
+    (96, 1024, 4, 64, 2, "f32", 0),
 ]
 
 
