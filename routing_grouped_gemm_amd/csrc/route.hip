@@ -63,7 +63,9 @@ __device__ __forceinline__ uint64_t segment_max(uint64_t x)
 // the VPL consecutive logits [l*VPL, l*VPL + VPL) (E <= LPT*VPL).  A block of
 // NTHR = min(TB * LPT, 1024) threads handles TB tokens, NTHR/LPT at a time
 // (all of them at once up to 16 lanes per token).
-template <int LPT, int VPL, int NTHR = (TB * LPT < 1024 ? (TB * LPT < 64 ? 64 : TB * LPT) : 1024)>
+// FULL: E == LPT * VPL, so every lane's logits lie inside the row (no
+// per-logit range test).
+template <int LPT, int VPL, int NTHR = (TB * LPT < 1024 ? (TB * LPT < 64 ? 64 : TB * LPT) : 1024), bool FULL = false>
 __global__ __launch_bounds__(NTHR) void route_topk_kernel(const float* __restrict__ logits, int T,
                                                          int E, int k, int nblk,
                                                          int32_t* __restrict__ topk_idx,
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(NTHR) void route_topk_kernel(const float* __restric
         const bool active = tl < nt;
         const int e0 = lane * VPL;
         float v[VPL];
-        if (vec && active && e0 + VPL <= E) {
+        if (vec && active && (FULL || e0 + VPL <= E)) {
             const float4* src = reinterpret_cast<const float4*>(logits + (int64_t)t * E + e0);
 #pragma unroll
             for (int s = 0; s < VPL / 4; ++s) {
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(NTHR) void route_topk_kernel(const float* __restric
         } else {
 #pragma unroll
             for (int s = 0; s < VPL; ++s)
-                v[s] = active && e0 + s < E ? logits[(int64_t)t * E + e0 + s] : -INFINITY;
+                v[s] = active && (FULL || e0 + s < E) ? logits[(int64_t)t * E + e0 + s] : -INFINITY;
         }
         // one 64-bit key per logit: the high word orders the fp32 values as
         // unsigned integers (-0 taken as +0, non-finite as -inf), the low
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(NTHR) void route_topk_kernel(const float* __restric
         uint64_t key[VPL];
 #pragma unroll
         for (int s = 0; s < VPL; ++s) {
-            const bool in = e0 + s < E;
+            const bool in = FULL || e0 + s < E;
             float x = v[s];
             if (active && in && !__builtin_isfinite(x)) bad = true;
             x = __builtin_isfinite(x) ? x : -INFINITY;
@@ -409,8 +411,12 @@ void launch_topk(int nblk, hipStream_t s, const float* logits, int T, int E, int
                  int32_t* topk_idx, float* topk_w, int32_t* hist, int32_t* dev_err)
 {
     constexpr int NTHR = TB * LPT < 1024 ? (TB * LPT < 64 ? 64 : TB * LPT) : 1024;
-    hipLaunchKernelGGL((route_topk_kernel<LPT, VPL, NTHR>), dim3(nblk), dim3(NTHR), 0, s, logits, T, E,
-                       k, nblk, topk_idx, topk_w, hist, dev_err);
+    if (E == LPT * VPL)
+        hipLaunchKernelGGL((route_topk_kernel<LPT, VPL, NTHR, true>), dim3(nblk), dim3(NTHR), 0, s, logits, T, E,
+                           k, nblk, topk_idx, topk_w, hist, dev_err);
+    else
+        hipLaunchKernelGGL((route_topk_kernel<LPT, VPL, NTHR>), dim3(nblk), dim3(NTHR), 0, s, logits, T, E,
+                           k, nblk, topk_idx, topk_w, hist, dev_err);
 }
 
 // Shared experts as extra groups: every token also takes slots k .. k+S-1,
